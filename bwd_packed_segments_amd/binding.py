@@ -1,0 +1,281 @@
+"""ctypes binding of libbps_attn.so (declared in include/bps_attn.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the computation runs in the library's
+HIP kernels.  There is no fallback: if the library is missing or a call
+fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_DEVICE = range(5)
+ATTN_BF16, ATTN_FP32 = 0, 1
+ATTN_FORCE_GENERAL = 1 << 0
+ATTN_REVERSE_SCHEDULE = 1 << 1
+ROUTE_NAMES = {0: "dense", 1: "fast", 2: "general"}
+
+STATUS_NAMES = {
+    ATTN_OK: "ATTN_OK", ATTN_E_INVALID: "ATTN_E_INVALID", ATTN_E_UNSUPPORTED: "ATTN_E_UNSUPPORTED",
+    ATTN_E_WORKSPACE: "ATTN_E_WORKSPACE", ATTN_E_DEVICE: "ATTN_E_DEVICE",
+}
+
+# Every symbol the header declares (the CPU tests check the library exports them).
+EXPORTS = ("attn_fwd_workspace_size", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
+           "attn_debug_mask", "attn_last_error", "attn_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class attn_strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("token", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+class attn_desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Sq", ctypes.c_int32), ("Skv", ctypes.c_int32),
+        ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("flags", ctypes.c_uint32),
+        ("q", attn_strides), ("k", attn_strides), ("v", attn_strides), ("o", attn_strides),
+    ]
+
+
+class attn_segments(ctypes.Structure):
+    _fields_ = [("ids_q", ctypes.c_void_p), ("pos_q", ctypes.c_void_p),
+                ("ids_kv", ctypes.c_void_p), ("pos_kv", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return os.environ.get("BPS_ATTN_LIB", os.path.join(_HERE, "libbps_attn.so"))
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m bwd_packed_segments_amd.build` "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(path)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        dp, sp = ctypes.POINTER(attn_desc), ctypes.POINTER(attn_segments)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.attn_fwd_workspace_size.argtypes = [dp, sp]
+        L.attn_fwd_workspace_size.restype = sz
+        L.attn_bwd_workspace_size.argtypes = [dp, sp]
+        L.attn_bwd_workspace_size.restype = sz
+        L.attn_fwd.argtypes = [dp, sp, vp, vp, vp, vp, vp, vp, sz, vp, i32p]
+        L.attn_fwd.restype = ctypes.c_int
+        L.attn_bwd.argtypes = [dp, sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i32p]
+        L.attn_bwd.restype = ctypes.c_int
+        L.attn_debug_mask.argtypes = [dp, sp, vp, vp, vp, sz, vp]
+        L.attn_debug_mask.restype = ctypes.c_int
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        L.attn_version.argtypes = []
+        L.attn_version.restype = ctypes.c_char_p
+        _lib = L
+        return L
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        msg = lib().attn_last_error().decode(errors="replace")
+        raise AttnError(status, msg)
+
+
+# ------------------------------------------------------------------ helpers
+
+def make_desc(*, B, Sq, Skv, Hq, Hkv, Dqk, Dv, dtype=ATTN_BF16, causal=False, scale=0.0, flags=0,
+              q=None, k=None, v=None, o=None) -> attn_desc:
+    """Descriptor with contiguous BSHD strides unless strides are given as
+    (batch, token, head) tuples."""
+    def st(given, S, H, D):
+        return attn_strides(*(given if given is not None else (S * H * D, H * D, D)))
+    return attn_desc(B, Sq, Skv, Hq, Hkv, Dqk, Dv, dtype, int(bool(causal)), float(scale), int(flags),
+                     st(q, Sq, Hq, Dqk), st(k, Skv, Hkv, Dqk), st(v, Skv, Hkv, Dv), st(o, Sq, Hq, Dv))
+
+
+@dataclass
+class Segments:
+    """THD metadata as device int32 tensors [B, S] (pos and kv parts optional)."""
+    ids_q: object
+    pos_q: object = None
+    ids_kv: object = None
+    pos_kv: object = None
+
+    def c(self) -> attn_segments:
+        def p(t):
+            if t is None:
+                return None
+            _require_device_int32(t)
+            return t.data_ptr()
+        return attn_segments(p(self.ids_q), p(self.pos_q), p(self.ids_kv), p(self.pos_kv))
+
+
+def _require_device_int32(t):
+    import torch
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()):
+        raise TypeError("segment metadata must be contiguous int32 device tensors")
+
+
+def _strides(t):
+    s = t.stride()
+    if s[3] != 1:
+        raise ValueError("the head-dim axis must be contiguous")
+    return (s[0], s[1], s[2])
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _require_device(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise TypeError("tensors must live in GPU memory")
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _desc_for(q, k, v, o_strides, causal, scale, flags):
+    B, Sq, Hq, Dqk = q.shape
+    Skv, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape[0] != B or v.shape[:3] != (B, Skv, Hkv) or k.shape[3] != Dqk:
+        raise ValueError("inconsistent q/k/v shapes")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    return make_desc(B=B, Sq=Sq, Skv=Skv, Hq=Hq, Hkv=Hkv, Dqk=Dqk, Dv=Dv, dtype=_dtype_code(q), causal=causal,
+                     scale=0.0 if scale is None else scale, flags=flags, q=_strides(q), k=_strides(k),
+                     v=_strides(v), o=o_strides)
+
+
+def _seg_ptr(segments):
+    if segments is None:
+        return None, None
+    cs = segments.c()
+    return cs, ctypes.byref(cs)
+
+
+def fwd_workspace_size(desc: attn_desc, segments: attn_segments | None = None) -> int:
+    return lib().attn_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(segments) if segments else None)
+
+
+def bwd_workspace_size(desc: attn_desc, segments: attn_segments | None = None) -> int:
+    return lib().attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(segments) if segments else None)
+
+
+def _workspace(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ public API
+
+def attn_fwd(q, k, v, *, causal=False, scale=None, segments: Segments | None = None, flags=0, out=None,
+             return_route=False):
+    """O [B,Sq,Hq,Dv] and LSE [B,Hq,Sq] (fp32) of fused attention."""
+    import torch
+    _require_device(q, k, v)
+    B, Sq, Hq, _ = q.shape
+    Dv = v.shape[3]
+    o = out if out is not None else torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
+    _require_device(o)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
+    cs, csp = _seg_ptr(segments)
+    L = lib()
+    ws_bytes = L.attn_fwd_workspace_size(ctypes.byref(desc), csp)
+    ws = _workspace(ws_bytes, q.device)
+    route = ctypes.c_int32(-1)
+    _check(L.attn_fwd(ctypes.byref(desc), csp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device), ctypes.byref(route)))
+    if return_route:
+        return o, lse, ROUTE_NAMES[route.value]
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segments | None = None, flags=0):
+    """dQ, dK, dV of fused attention from the saved O and LSE."""
+    import torch
+    _require_device(q, k, v, o, lse, do)
+    if do.stride() != o.stride() or do.shape != o.shape:
+        raise ValueError("dO must have the shape and strides of O")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        dq, dk, dv = (torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device) for t in (q, k, v))
+    desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
+    cs, csp = _seg_ptr(segments)
+    L = lib()
+    ws_bytes = L.attn_bwd_workspace_size(ctypes.byref(desc), csp)
+    ws = _workspace(ws_bytes, q.device)
+    _check(L.attn_bwd(ctypes.byref(desc), csp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      ws.data_ptr(), ws.numel(), _stream(q.device), None))
+    return dq, dk, dv
+
+
+def attn_debug_mask(*, B, Sq, Skv, causal=False, segments: Segments | None = None, flags=0, device="cuda"):
+    """The mask the kernels apply (uint8 [B,Sq,Skv]) and each row's route."""
+    import torch
+    desc = make_desc(B=B, Sq=Sq, Skv=Skv, Hq=1, Hkv=1, Dqk=64, Dv=64, causal=causal, flags=flags)
+    cs, csp = _seg_ptr(segments)
+    L = lib()
+    ws = _workspace(L.attn_fwd_workspace_size(ctypes.byref(desc), csp), device)
+    mask = torch.empty((B, Sq, Skv), dtype=torch.uint8, device=device)
+    routes = torch.empty((B,), dtype=torch.int32, device=device)
+    _check(L.attn_debug_mask(ctypes.byref(desc), csp, mask.data_ptr(), routes.data_ptr(), ws.data_ptr(),
+                             ws.numel(), _stream(torch.device(device))))
+    return mask, routes
+
+
+def validate_fwd(desc: attn_desc, segments: attn_segments | None = None, *, q=1 << 12, k=1 << 12, v=1 << 12,
+                 o=1 << 12, lse=1 << 12, ws=None, ws_bytes=0):
+    """Call attn_fwd with placeholder addresses to exercise host validation.
+    Only for descriptors that must fail validation (nothing may launch);
+    returns (status, message)."""
+    L = lib()
+    st = L.attn_fwd(ctypes.byref(desc), ctypes.byref(segments) if segments else None, q, k, v, o, lse, ws,
+                    ws_bytes, None, None)
+    return st, L.attn_last_error().decode(errors="replace")
+
+
+def validate_bwd(desc: attn_desc, segments: attn_segments | None = None, *, ptr=1 << 12, ws=None, ws_bytes=0,
+                 dq=...):
+    """attn_bwd counterpart of validate_fwd (same restriction)."""
+    L = lib()
+    dqp = ptr if dq is ... else dq
+    st = L.attn_bwd(ctypes.byref(desc), ctypes.byref(segments) if segments else None, ptr, ptr, ptr, ptr, ptr,
+                    ptr, dqp, ptr, ptr, ws, ws_bytes, None, None)
+    return st, L.attn_last_error().decode(errors="replace")

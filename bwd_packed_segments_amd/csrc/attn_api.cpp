@@ -1,0 +1,370 @@
+// C ABI of the attention library: host-side validation, workspace layout,
+// route choice and kernel launches.  Validation makes no HIP call, so every
+// argument error is reported (and nothing launched) even without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bps_args.hpp"
+#include "bps_attn.h"
+
+namespace {
+
+using bps::ChunkSum;
+
+thread_local std::string g_err;
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Plan {
+  bool meta = false;
+  int sides = 0;
+  bool fast_candidate = false;
+  bool check_eq = false;
+  bool derive_pos_q = false, derive_pos_kv = false;
+  int nch_q = 0, nch_kv = 0;
+  float scale = 0.f;
+  size_t off_route = 0, off_run_q = 0, off_pos_q = 0, off_sum_q = 0;
+  size_t off_run_kv = 0, off_pos_kv = 0, off_sum_kv = 0;
+  size_t off_delta = 0, off_lse2 = 0;
+  size_t ws_fwd = 0, ws_bwd = 0;
+};
+
+bool supported_dims(int dtype, int dqk, int dv) {
+  if (dtype == ATTN_BF16) return (dqk == 64 || dqk == 128 || dqk == 192) && (dv == 64 || dv == 128);
+  if (dtype == ATTN_FP32) return (dqk == 64 || dqk == 128) && (dv == 64 || dv == 128);
+  return false;
+}
+
+attn_status check_strides(const char* name, const attn_strides& s, int vec) {
+  if (s.batch < 0 || s.token < 0 || s.head < 0)
+    return fail(ATTN_E_INVALID, "%s strides must be non-negative", name);
+  if (s.batch % vec || s.token % vec || s.head % vec)
+    return fail(ATTN_E_UNSUPPORTED, "%s strides must be multiples of %d elements (16-byte rows)", name, vec);
+  return ATTN_OK;
+}
+
+attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
+  if (!d) return fail(ATTN_E_INVALID, "desc is NULL");
+  if (d->B < 1 || d->Sq < 0 || d->Skv < 0 || d->Hq < 1 || d->Hkv < 1 || d->Dqk < 1 || d->Dv < 1)
+    return fail(ATTN_E_INVALID, "sizes must be positive (B=%d Sq=%d Skv=%d Hq=%d Hkv=%d Dqk=%d Dv=%d)", d->B,
+                d->Sq, d->Skv, d->Hq, d->Hkv, d->Dqk, d->Dv);
+  if (d->Hq % d->Hkv) return fail(ATTN_E_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", d->Hq, d->Hkv);
+  if (d->dtype != ATTN_BF16 && d->dtype != ATTN_FP32) return fail(ATTN_E_INVALID, "unknown dtype %d", d->dtype);
+  if (!supported_dims(d->dtype, d->Dqk, d->Dv))
+    return fail(ATTN_E_UNSUPPORTED, "head dims (Dqk=%d, Dv=%d) not built for dtype %d", d->Dqk, d->Dv, d->dtype);
+  if (d->causal != 0 && d->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
+  if (!std::isfinite(d->scale) || d->scale < 0.f) return fail(ATTN_E_INVALID, "scale must be finite and >= 0");
+  if (d->flags & ~static_cast<uint32_t>(ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE))
+    return fail(ATTN_E_INVALID, "unknown flag bits 0x%x", d->flags);
+  const long long rows = (long long)d->B * d->Hq * (long long)(d->Sq > d->Skv ? d->Sq : d->Skv);
+  if (rows > (1LL << 31) - 1) return fail(ATTN_E_UNSUPPORTED, "B*H*S exceeds 2^31");
+  const int vec = d->dtype == ATTN_BF16 ? 8 : 4;
+  attn_status st;
+  if ((st = check_strides("q", d->q, vec)) != ATTN_OK) return st;
+  if ((st = check_strides("k", d->k, vec)) != ATTN_OK) return st;
+  if ((st = check_strides("v", d->v, vec)) != ATTN_OK) return st;
+  if ((st = check_strides("o", d->o, vec)) != ATTN_OK) return st;
+  p->scale = d->scale == 0.f ? 1.f / std::sqrt(static_cast<float>(d->Dqk)) : d->scale;
+
+  p->meta = seg != nullptr;
+  if (!p->meta) {
+    if (d->causal && d->Sq != d->Skv)
+      return fail(ATTN_E_UNSUPPORTED, "causal attention without segment metadata needs Sq == Skv (%d != %d)",
+                  d->Sq, d->Skv);
+  } else {
+    if (!seg->ids_q) return fail(ATTN_E_INVALID, "segment metadata given without ids_q");
+    if (!seg->ids_kv && seg->pos_kv)
+      return fail(ATTN_E_INVALID, "pos_kv given without ids_kv (ids and pos must come in pairs)");
+    const bool self = !seg->ids_kv || (seg->ids_kv == seg->ids_q && seg->pos_kv == seg->pos_q);
+    if (self && d->Sq != d->Skv)
+      return fail(ATTN_E_INVALID, "self-attention metadata (no separate ids_kv) needs Sq == Skv (%d != %d)",
+                  d->Sq, d->Skv);
+    p->sides = self ? 1 : 2;
+    const bool forced = (d->flags & ATTN_FORCE_GENERAL) != 0;
+    p->check_eq = !self && d->Sq == d->Skv && !forced;
+    p->fast_candidate = !forced && (self || p->check_eq);
+    p->derive_pos_q = seg->pos_q == nullptr;
+    p->derive_pos_kv = !self && seg->pos_kv == nullptr;
+    p->nch_q = (d->Sq + bps::kChunk - 1) / bps::kChunk;
+    p->nch_kv = (d->Skv + bps::kChunk - 1) / bps::kChunk;
+  }
+
+  size_t off = 0;
+  if (p->meta) {
+    const size_t B = d->B;
+    p->off_route = off; off = align_up(off + B * sizeof(int));
+    p->off_run_q = off; off = align_up(off + B * d->Sq * sizeof(int2));
+    if (p->derive_pos_q) { p->off_pos_q = off; off = align_up(off + B * d->Sq * sizeof(int)); }
+    p->off_sum_q = off; off = align_up(off + B * p->nch_q * sizeof(ChunkSum));
+    if (p->sides == 2) {
+      p->off_run_kv = off; off = align_up(off + B * d->Skv * sizeof(int2));
+      if (p->derive_pos_kv) { p->off_pos_kv = off; off = align_up(off + B * d->Skv * sizeof(int)); }
+      p->off_sum_kv = off; off = align_up(off + B * p->nch_kv * sizeof(ChunkSum));
+    }
+  }
+  p->ws_fwd = off;
+  const size_t nrow = (size_t)d->B * d->Hq * d->Sq;
+  p->off_delta = off; off = align_up(off + nrow * sizeof(float));
+  p->off_lse2 = off; off = align_up(off + nrow * sizeof(float));
+  p->ws_bwd = off;
+  return ATTN_OK;
+}
+
+bool need_nonnull(const void* ptr, long long elems) { return elems > 0 && ptr == nullptr; }
+
+bps::Strides strides_of(const attn_strides& s) { return bps::Strides{s.batch, s.token, s.head}; }
+
+bps::AttnShape shape_of(const attn_desc* d, const Plan& p) {
+  bps::AttnShape s;
+  s.B = d->B; s.Sq = d->Sq; s.Skv = d->Skv; s.Hq = d->Hq; s.Hkv = d->Hkv;
+  s.causal = d->causal;
+  s.reverse = (d->flags & ATTN_REVERSE_SCHEDULE) ? 1 : 0;
+  s.has_meta = p.meta ? 1 : 0;
+  s.scale = p.scale;
+  s.scale_log2 = p.scale * bps::kLog2e;
+  return s;
+}
+
+// Launches the metadata preparation and fills the kernels' view of it.
+attn_status prepare_segments(const attn_desc* d, const attn_segments* seg, const Plan& p, char* ws,
+                             hipStream_t st, bps::SegView* view) {
+  *view = bps::SegView{};
+  if (!p.meta) return ATTN_OK;
+  bps::SegMetaArgs m{};
+  m.B = d->B; m.Sq = d->Sq; m.Skv = d->Skv;
+  m.sides = p.sides;
+  m.check_eq = p.check_eq ? 1 : 0;
+  m.force_general = (d->flags & ATTN_FORCE_GENERAL) ? 1 : 0;
+  m.ids[0] = seg->ids_q;
+  m.pos_in[0] = seg->pos_q;
+  m.pos_out[0] = p.derive_pos_q ? reinterpret_cast<int*>(ws + p.off_pos_q) : nullptr;
+  m.run[0] = reinterpret_cast<int2*>(ws + p.off_run_q);
+  m.sum[0] = reinterpret_cast<ChunkSum*>(ws + p.off_sum_q);
+  m.nch[0] = p.nch_q;
+  if (p.sides == 2) {
+    m.ids[1] = seg->ids_kv;
+    m.pos_in[1] = seg->pos_kv;
+    m.pos_out[1] = p.derive_pos_kv ? reinterpret_cast<int*>(ws + p.off_pos_kv) : nullptr;
+    m.run[1] = reinterpret_cast<int2*>(ws + p.off_run_kv);
+    m.sum[1] = reinterpret_cast<ChunkSum*>(ws + p.off_sum_kv);
+    m.nch[1] = p.nch_kv;
+  } else {
+    m.ids[1] = m.ids[0];
+    m.pos_in[1] = m.pos_in[0];
+    m.pos_out[1] = nullptr;
+    m.run[1] = m.run[0];
+    m.sum[1] = m.sum[0];
+    m.nch[1] = m.nch[0];
+  }
+  m.route = reinterpret_cast<int*>(ws + p.off_route);
+
+  view->ids_q = seg->ids_q;
+  view->pos_q = p.derive_pos_q ? m.pos_out[0] : seg->pos_q;
+  view->run_q = m.run[0];
+  view->sum_q = m.sum[0];
+  view->nch_q = p.nch_q;
+  if (p.sides == 2) {
+    view->ids_kv = seg->ids_kv;
+    view->pos_kv = p.derive_pos_kv ? m.pos_out[1] : seg->pos_kv;
+    view->run_kv = m.run[1];
+    view->sum_kv = m.sum[1];
+    view->nch_kv = p.nch_kv;
+  } else {
+    view->ids_kv = view->ids_q;
+    view->pos_kv = view->pos_q;
+    view->run_kv = view->run_q;
+    view->sum_kv = view->sum_q;
+    view->nch_kv = view->nch_q;
+  }
+  view->route = m.route;
+  if (d->B == 0 || (d->Sq == 0 && d->Skv == 0)) return ATTN_OK;
+  hipError_t e = bps::launch_seg_meta(m, st);
+  if (e != hipSuccess) return fail(ATTN_E_DEVICE, "segment metadata kernel: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+template <typename T>
+hipError_t dispatch_fwd(int dqk, int dv, const bps::FwdArgs& a, hipStream_t st) {
+  if (dqk == 64 && dv == 64) return bps::launch_fwd<T, 64, 64>(a, st);
+  if (dqk == 64 && dv == 128) return bps::launch_fwd<T, 64, 128>(a, st);
+  if (dqk == 128 && dv == 64) return bps::launch_fwd<T, 128, 64>(a, st);
+  if (dqk == 128 && dv == 128) return bps::launch_fwd<T, 128, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+template <typename T>
+hipError_t dispatch_bwd(int dqk, int dv, const bps::BwdArgs& a, hipStream_t st) {
+  if (dqk == 64 && dv == 64) return bps::launch_bwd<T, 64, 64>(a, st);
+  if (dqk == 64 && dv == 128) return bps::launch_bwd<T, 64, 128>(a, st);
+  if (dqk == 128 && dv == 64) return bps::launch_bwd<T, 128, 64>(a, st);
+  if (dqk == 128 && dv == 128) return bps::launch_bwd<T, 128, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+template <>
+hipError_t dispatch_fwd<bps::bf16>(int dqk, int dv, const bps::FwdArgs& a, hipStream_t st) {
+  using T = bps::bf16;
+  if (dqk == 64 && dv == 64) return bps::launch_fwd<T, 64, 64>(a, st);
+  if (dqk == 64 && dv == 128) return bps::launch_fwd<T, 64, 128>(a, st);
+  if (dqk == 128 && dv == 64) return bps::launch_fwd<T, 128, 64>(a, st);
+  if (dqk == 128 && dv == 128) return bps::launch_fwd<T, 128, 128>(a, st);
+  if (dqk == 192 && dv == 64) return bps::launch_fwd<T, 192, 64>(a, st);
+  if (dqk == 192 && dv == 128) return bps::launch_fwd<T, 192, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+template <>
+hipError_t dispatch_bwd<bps::bf16>(int dqk, int dv, const bps::BwdArgs& a, hipStream_t st) {
+  using T = bps::bf16;
+  if (dqk == 64 && dv == 64) return bps::launch_bwd<T, 64, 64>(a, st);
+  if (dqk == 64 && dv == 128) return bps::launch_bwd<T, 64, 128>(a, st);
+  if (dqk == 128 && dv == 64) return bps::launch_bwd<T, 128, 64>(a, st);
+  if (dqk == 128 && dv == 128) return bps::launch_bwd<T, 128, 128>(a, st);
+  if (dqk == 192 && dv == 64) return bps::launch_bwd<T, 192, 64>(a, st);
+  if (dqk == 192 && dv == 128) return bps::launch_bwd<T, 192, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+int route_of(const Plan& p) {
+  if (!p.meta) return ATTN_ROUTE_DENSE;
+  return p.fast_candidate ? ATTN_ROUTE_FAST : ATTN_ROUTE_GENERAL;
+}
+
+attn_status check_ws(void* ws, size_t have, size_t need) {
+  if (have < need) return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", have, need);
+  if (need > 0 && ws == nullptr) return fail(ATTN_E_WORKSPACE, "workspace pointer is NULL (%zu bytes required)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(ATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
+  return ATTN_OK;
+}
+
+attn_status check_align(const char* name, const void* ptr, int dtype) {
+  (void)dtype;
+  if (reinterpret_cast<uintptr_t>(ptr) % 16)
+    return fail(ATTN_E_UNSUPPORTED, "%s must be 16-byte aligned", name);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_fwd_workspace_size(const attn_desc* desc, const attn_segments* seg) {
+  Plan p;
+  return make_plan(desc, seg, &p) == ATTN_OK ? p.ws_fwd : 0;
+}
+
+size_t attn_bwd_workspace_size(const attn_desc* desc, const attn_segments* seg) {
+  Plan p;
+  return make_plan(desc, seg, &p) == ATTN_OK ? p.ws_bwd : 0;
+}
+
+attn_status attn_fwd(const attn_desc* d, const attn_segments* seg, const void* q, const void* k, const void* v,
+                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                     int32_t* route_out) {
+  try {
+    Plan p;
+    attn_status st = make_plan(d, seg, &p);
+    if (st != ATTN_OK) return st;
+    const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
+    if (need_nonnull(q, nq) || need_nonnull(o, nq) || need_nonnull(lse, nq))
+      return fail(ATTN_E_INVALID, "q, o and lse must not be NULL");
+    if (need_nonnull(k, nkv) || need_nonnull(v, nkv)) return fail(ATTN_E_INVALID, "k and v must not be NULL");
+    if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
+        (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)))
+      return st;
+    if ((st = check_ws(workspace, workspace_bytes, p.ws_fwd)) != ATTN_OK) return st;
+    if (route_out) *route_out = route_of(p);
+    if (d->Sq == 0) return ATTN_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    bps::FwdArgs a{};
+    a.s = shape_of(d, p);
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
+    if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg)) != ATTN_OK) return st;
+    hipError_t e = d->dtype == ATTN_BF16 ? dispatch_fwd<bps::bf16>(d->Dqk, d->Dv, a, hs)
+                                         : dispatch_fwd<float>(d->Dqk, d->Dv, a, hs);
+    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "forward launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
+}
+
+attn_status attn_bwd(const attn_desc* d, const attn_segments* seg, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream, int32_t* route_out) {
+  try {
+    Plan p;
+    attn_status st = make_plan(d, seg, &p);
+    if (st != ATTN_OK) return st;
+    const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
+    if (need_nonnull(q, nq) || need_nonnull(o, nq) || need_nonnull(lse, nq) || need_nonnull(dout, nq) ||
+        need_nonnull(dq, nq))
+      return fail(ATTN_E_INVALID, "q, o, lse, dout and dq must not be NULL");
+    if (need_nonnull(k, nkv) || need_nonnull(v, nkv) || need_nonnull(dk, nkv) || need_nonnull(dv, nkv))
+      return fail(ATTN_E_INVALID, "k, v, dk and dv must not be NULL");
+    if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
+        (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)) ||
+        (st = check_align("dout", dout, d->dtype)) || (st = check_align("dq", dq, d->dtype)) ||
+        (st = check_align("dk", dk, d->dtype)) || (st = check_align("dv", dv, d->dtype)))
+      return st;
+    if ((st = check_ws(workspace, workspace_bytes, p.ws_bwd)) != ATTN_OK) return st;
+    if (route_out) *route_out = route_of(p);
+    if (d->Sq == 0 && d->Skv == 0) return ATTN_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    bps::BwdArgs a{};
+    a.s = shape_of(d, p);
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
+    a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_delta);
+    a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_lse2);
+    if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg)) != ATTN_OK) return st;
+    hipError_t e = d->dtype == ATTN_BF16 ? dispatch_bwd<bps::bf16>(d->Dqk, d->Dv, a, hs)
+                                         : dispatch_bwd<float>(d->Dqk, d->Dv, a, hs);
+    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "backward launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
+}
+
+attn_status attn_debug_mask(const attn_desc* d, const attn_segments* seg, uint8_t* mask_out, int32_t* route_rows,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    Plan p;
+    attn_status st = make_plan(d, seg, &p);
+    if (st != ATTN_OK) return st;
+    if (need_nonnull(mask_out, (long long)d->B * d->Sq * d->Skv))
+      return fail(ATTN_E_INVALID, "mask_out must not be NULL");
+    if ((st = check_ws(workspace, workspace_bytes, p.ws_fwd)) != ATTN_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    bps::MaskArgs a{};
+    a.B = d->B; a.Sq = d->Sq; a.Skv = d->Skv; a.causal = d->causal; a.has_meta = p.meta ? 1 : 0;
+    a.mask = mask_out;
+    a.route_rows = route_rows;
+    if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg)) != ATTN_OK) return st;
+    hipError_t e = bps::launch_debug_mask(a, hs);
+    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "mask launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
+}
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+const char* attn_version(void) { return "bps_attn 0.1 (gfx950)"; }
+
+}  // extern "C"

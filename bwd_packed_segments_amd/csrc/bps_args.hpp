@@ -1,0 +1,84 @@
+// Kernel argument blocks and launcher declarations shared by the host
+// dispatcher (attn_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bps_common.hpp"
+
+namespace bps {
+
+struct Strides {
+  int64_t b, t, h;   // elements
+};
+
+struct AttnShape {
+  int B, Sq, Skv, Hq, Hkv;
+  int causal;
+  int reverse;       // reverse the workgroup schedule
+  int has_meta;
+  float scale;       // softmax scale (natural)
+  float scale_log2;  // scale * log2(e)
+};
+
+struct FwdArgs {
+  AttnShape s;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  Strides sq, sk, sv, so;
+  SegView seg;
+};
+
+struct BwdArgs {
+  AttnShape s;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  Strides sq, sk, sv, so;
+  float* delta;      // [B, Hq, Sq] workspace: rowsum(dO * O)
+  float* lse2;       // [B, Hq, Sq] workspace: LSE * log2(e), +inf for empty rows
+  SegView seg;
+};
+
+struct SegMetaArgs {
+  int B, Sq, Skv;
+  int sides;          // 1: KV metadata are Q's; 2: separate KV metadata
+  int check_eq;       // compare Q and KV metadata elementwise (side 0)
+  int force_general;
+  const int* ids[2];
+  const int* pos_in[2];   // NULL: derive from ids
+  int* pos_out[2];        // derived positions (when pos_in is NULL)
+  int2* run[2];
+  ChunkSum* sum[2];
+  int nch[2];
+  int* route;             // [B]
+};
+
+struct MaskArgs {
+  int B, Sq, Skv, causal, has_meta;
+  SegView seg;
+  uint8_t* mask;    // [B, Sq, Skv]
+  int* route_rows;  // [B] or NULL
+};
+
+// Launchers (defined in the kernel translation units).  Each returns the
+// result of hipGetLastError() after its launches.
+hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st);
+hipError_t launch_debug_mask(const MaskArgs& a, hipStream_t st);
+
+template <typename T, int DQK, int DV>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
+template <typename T, int DQK, int DV>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+
+}  // namespace bps

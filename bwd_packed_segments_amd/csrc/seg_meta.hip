@@ -1,0 +1,237 @@
+// Segment metadata preparation (runs before every attention kernel that has
+// THD metadata) and the mask dump used by the tests.
+//
+// Per batch row and per side (Q, and KV when its metadata are separate) one
+// 1024-thread workgroup scans the row of segment ids:
+//   * run start and end of every token's contiguous id run (the device form
+//     of the cu_seqlens-style ragged offsets of TransformerEngine PR 2358,
+//     review of the ragged offset tensor); (0, 0) for padding (id 0);
+//   * positions derived from ids when none are given (offset inside the run,
+//     the helper of "[JAX] Fix batcher in FusedAttn primitive ...",
+//     Description);
+//   * one summary per 32 tokens (ids, positions, run bounds of the tokens
+//     with a nonzero id) used by the kernels to skip or fully accept tiles;
+//   * on the Q side, whether the fast (boundary-only) route is exact for the
+//     row: Q and KV metadata equal, runs of nonzero ids increasing, positions
+//     equal to run offsets ("[JAX] Align fused attn backward output gradient
+//     sharding ...", Changes 3 and 4).  The route can only fall back to the
+//     general path here, never the other way.
+#include "bps_args.hpp"
+
+namespace bps {
+
+namespace {
+
+constexpr int kSegThreads = 1024;
+constexpr int kSegItems = 8;
+constexpr int kSegRound = kSegThreads * kSegItems;
+constexpr int kSegWaves = kSegThreads / 64;
+
+__device__ inline int op_max(int a, int b) { return a > b ? a : b; }
+__device__ inline int op_min(int a, int b) { return a < b ? a : b; }
+
+// Exclusive scan over the threads of the workgroup: forward combines the
+// values of threads before this one, reverse those after it.  Returns the
+// exclusive result and stores the combination of all threads in *total.
+template <bool MAXOP, bool REVERSE>
+__device__ int block_excl_scan(int v, int* wsum, int identity, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = REVERSE ? __shfl_down(x, d) : __shfl_up(x, d);
+    bool take = REVERSE ? (lane + d < 64) : (lane >= d);
+    if (take) x = MAXOP ? op_max(x, y) : op_min(x, y);
+  }
+  int excl = REVERSE ? __shfl_down(x, 1) : __shfl_up(x, 1);
+  if (REVERSE ? (lane == 63) : (lane == 0)) excl = identity;
+  if (REVERSE ? (lane == 0) : (lane == 63)) wsum[wave] = x;
+  __syncthreads();
+  int pre = identity, tot = identity;
+#pragma unroll
+  for (int w = 0; w < kSegWaves; ++w) {
+    int s = wsum[w];
+    tot = MAXOP ? op_max(tot, s) : op_min(tot, s);
+    if (REVERSE ? (w > wave) : (w < wave)) pre = MAXOP ? op_max(pre, s) : op_min(pre, s);
+  }
+  __syncthreads();
+  *total = tot;
+  return MAXOP ? op_max(pre, excl) : op_min(pre, excl);
+}
+
+__global__ __launch_bounds__(kSegThreads) void seg_meta_kernel(SegMetaArgs a) {
+  const int b = blockIdx.x;
+  const int side = blockIdx.y;
+  const int S = side ? a.Skv : a.Sq;
+  const size_t row = (size_t)b * S;
+  const int* ids = a.ids[side] + row;
+  const int* pos_in = a.pos_in[side] ? a.pos_in[side] + row : nullptr;
+  int* pos_out = a.pos_out[side] ? a.pos_out[side] + row : nullptr;
+  int2* run = a.run[side] + row;
+  ChunkSum* sum = a.sum[side] + (size_t)b * a.nch[side];
+  const int nch = a.nch[side];
+  const bool eq_check = side == 0 && a.check_eq;
+  const int* ids_kv = eq_check ? a.ids[1] + row : nullptr;
+  const int* pos_kv = (eq_check && a.pos_in[1]) ? a.pos_in[1] + row : nullptr;
+
+  __shared__ int wsum[4][kSegWaves];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  int ok = 1;
+  int carry_start = -1;
+  int carry_nz = INT32_MIN;
+  const int nrounds = (S + kSegRound - 1) / kSegRound;
+
+  // Phase 1, left to right: run starts, derived positions, fast-route checks.
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int base = rd * kSegRound + t * kSegItems;
+    int id[kSegItems];
+    int st[kSegItems];
+    int prev = (base > 0 && base - 1 < S) ? ids[base - 1] : 0;
+    int st_local = -1;
+    int nz_local = INT32_MIN;
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k) {
+      const int i = base + k;
+      const bool in = i < S;
+      id[k] = in ? ids[i] : 0;
+      const int pid = k == 0 ? prev : id[k - 1];
+      if (in && (i == 0 || id[k] != pid)) st_local = i;
+      st[k] = st_local;
+      if (in && id[k] != 0) nz_local = op_max(nz_local, id[k]);
+    }
+    int tot;
+    const int pre_start = op_max(carry_start, block_excl_scan<true, false>(st_local, wsum[0], -1, &tot));
+    carry_start = op_max(carry_start, tot);
+    const int pre_nz = op_max(carry_nz, block_excl_scan<true, false>(nz_local, wsum[1], INT32_MIN, &tot));
+    carry_nz = op_max(carry_nz, tot);
+    bool seen_nz = pre_nz != INT32_MIN;
+    int running_nz = pre_nz;
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k) {
+      const int i = base + k;
+      if (i >= S) break;
+      const int rs = st[k] >= 0 ? st[k] : pre_start;
+      const int dpos = i - rs;
+      if (id[k] != 0) {
+        if (id[k] == INT32_MIN) ok = 0;
+        if (rs == i && seen_nz && id[k] <= running_nz) ok = 0;
+        running_nz = seen_nz ? op_max(running_nz, id[k]) : id[k];
+        seen_nz = true;
+      }
+      const int p = pos_in ? pos_in[i] : dpos;
+      if (pos_in && id[k] != 0 && p != dpos) ok = 0;
+      if (pos_out) pos_out[i] = dpos;
+      if (eq_check) {
+        const int pk = pos_kv ? pos_kv[i] : dpos;
+        if (ids_kv[i] != id[k] || pk != p) ok = 0;
+      }
+      run[i] = make_int2(rs, 0);
+    }
+  }
+
+  // Phase 2, right to left: run ends, final run bounds, 32-token summaries.
+  int carry_end = INT32_MAX;
+  for (int rd = nrounds - 1; rd >= 0; --rd) {
+    const int base = rd * kSegRound + t * kSegItems;
+    int id[kSegItems];
+    int en[kSegItems];
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k) id[k] = (base + k < S) ? ids[base + k] : 0;
+    const int next = (base + kSegItems < S) ? ids[base + kSegItems] : 0;
+    int en_local = INT32_MAX;
+#pragma unroll
+    for (int k = kSegItems - 1; k >= 0; --k) {
+      const int i = base + k;
+      if (i < S) {
+        const int nid = k == kSegItems - 1 ? next : id[k + 1];
+        if (i == S - 1 || id[k] != nid) en_local = i + 1;
+      }
+      en[k] = en_local;
+    }
+    int tot;
+    const int pre_end = op_min(carry_end, block_excl_scan<false, true>(en_local, wsum[2], INT32_MAX, &tot));
+    carry_end = op_min(carry_end, tot);
+
+    int cnt = 0, idmin = INT32_MAX, idmax = INT32_MIN, pmin = INT32_MAX, pmax = INT32_MIN;
+    int smin = INT32_MAX, smax = INT32_MIN, emin = INT32_MAX, emax = INT32_MIN;
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k) {
+      const int i = base + k;
+      if (i >= S) break;
+      if (id[k] == 0) {
+        run[i] = make_int2(0, 0);
+        continue;
+      }
+      const int rs = run[i].x;
+      const int re = en[k] != INT32_MAX ? en[k] : pre_end;
+      run[i] = make_int2(rs, re);
+      const int p = pos_in ? pos_in[i] : i - rs;
+      ++cnt;
+      idmin = op_min(idmin, id[k]); idmax = op_max(idmax, id[k]);
+      pmin = op_min(pmin, p); pmax = op_max(pmax, p);
+      smin = op_min(smin, rs); smax = op_max(smax, rs);
+      emin = op_min(emin, re); emax = op_max(emax, re);
+    }
+    // 4 consecutive threads cover one 32-token chunk.
+#pragma unroll
+    for (int d = 1; d < 4; d <<= 1) {
+      cnt += __shfl_xor(cnt, d);
+      idmin = op_min(idmin, __shfl_xor(idmin, d)); idmax = op_max(idmax, __shfl_xor(idmax, d));
+      pmin = op_min(pmin, __shfl_xor(pmin, d)); pmax = op_max(pmax, __shfl_xor(pmax, d));
+      smin = op_min(smin, __shfl_xor(smin, d)); smax = op_max(smax, __shfl_xor(smax, d));
+      emin = op_min(emin, __shfl_xor(emin, d)); emax = op_max(emax, __shfl_xor(emax, d));
+    }
+    const int chunk = (rd * kSegRound + t * kSegItems) / kChunk;
+    if ((lane & 3) == 0 && chunk < nch) {
+      ChunkSum c;
+      c.cnt = cnt; c.idmin = idmin; c.idmax = idmax; c.posmin = pmin;
+      c.posmax = pmax; c.smin = smin; c.smax = smax; c.emin = emin;
+      c.emax = emax; c.pad0 = 0; c.pad1 = 0; c.pad2 = 0;
+      sum[chunk] = c;
+    }
+  }
+
+  const int all_ok = __syncthreads_and(ok);
+  if (side == 0 && t == 0) {
+    const bool fast_candidate = !a.force_general && (a.sides == 1 || a.check_eq);
+    a.route[b] = (fast_candidate && all_ok) ? kRouteFast : kRouteGeneral;
+  }
+}
+
+__global__ __launch_bounds__(256) void debug_mask_kernel(MaskArgs a) {
+  const size_t total = (size_t)a.B * a.Sq * a.Skv;
+  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < total; x += (size_t)gridDim.x * blockDim.x) {
+    const int j = (int)(x % a.Skv);
+    const int i = (int)((x / a.Skv) % a.Sq);
+    const int b = (int)(x / ((size_t)a.Skv * a.Sq));
+    const int route = a.has_meta ? a.seg.route[b] : kRouteDense;
+    TokMeta qi = q_meta(route, a.seg, b, a.Sq, i);
+    TokMeta kj = route == kRouteGeneral ? kv_meta(route, a.seg, b, a.Skv, j) : TokMeta{0, 0};
+    a.mask[x] = allowed(route, a.causal != 0, a.Skv, i, j, qi, kj) ? 1 : 0;
+  }
+  if (a.route_rows && blockIdx.x == 0) {
+    for (int b = threadIdx.x; b < a.B; b += blockDim.x)
+      a.route_rows[b] = a.has_meta ? a.seg.route[b] : kRouteDense;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st) {
+  dim3 grid(a.B, a.sides);
+  hipLaunchKernelGGL(seg_meta_kernel, grid, dim3(kSegThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_mask(const MaskArgs& a, hipStream_t st) {
+  const size_t total = (size_t)a.B * a.Sq * a.Skv;
+  size_t blocks = (total + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(debug_mask_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace bps

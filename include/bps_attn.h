@@ -1,0 +1,174 @@
+/*
+ * bps_attn.h - C ABI of the MI355X (gfx950) fused attention library,
+ * forward and backward, over packed variable-length (THD) sequences.
+ *
+ * What it computes (the operation named by "[JAX] Align fused attn backward
+ * output gradient sharding and other test strengthening", TransformerEngine
+ * PR 3516, Diagram: the fused-attention forward saves its output, the
+ * backward turns it and the output gradient into Q/K/V gradients):
+ *
+ *   S_ij = scale * <q_i, k_j>,  allowed(i, j) decided by the mask below,
+ *   P_ij = softmax_j over allowed j,   O_i = sum_j P_ij v_j,
+ *   LSE_i = log sum_{allowed j} exp(S_ij)           (natural log),
+ *   dV_j = sum_i P_ij dO_i,   dP_ij = <dO_i, v_j>,  Delta_i = <dO_i, O_i>,
+ *   dS_ij = P_ij (dP_ij - Delta_i),
+ *   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
+ *
+ * With grouped-query attention (Hq = g * Hkv) query head h reads key/value
+ * head h / g, and dK, dV of a key/value head sum over the g query heads of
+ * its group (maxdiffusion PR 485, Code Review and Key Features of the fused
+ * backward: q_heads_per_kv_head, dK/dV accumulated across GQA heads).  Query
+ * and value head dims may differ (TransformerEngine PR 2358, review of the
+ * KV-packed stride: qk_head_dim vs v_head_dim).
+ *
+ * Mask.  Without segment metadata every pair is allowed, or j <= i when
+ * causal (then Sq must equal Skv).  With metadata, each token carries a
+ * segment id and a position inside its segment, separately for Q and KV
+ * ("[JAX] Fix batcher in FusedAttn primitive for when seg ids bdims != seg
+ * pos bdims", TransformerEngine PR 2692, Description); query i may attend
+ * key j when ids_q[i] == ids_kv[j] != 0 and, when causal,
+ * pos_kv[j] <= pos_q[i].  Id 0 is padding.  A query that attends nothing
+ * gets O = 0, LSE = -inf and dQ = 0; a key that nobody attends gets
+ * dK = dV = 0 (every output element is written, so callers need no memset;
+ * cf. the gradient zeroing for ragged layouts in TransformerEngine PR 2358,
+ * Greptile Overview).
+ *
+ * Routes.  When Q and KV metadata match, each nonzero id is one contiguous
+ * run (runs of nonzero ids have increasing ids) and pos is the offset inside
+ * the run, the kernels decide the mask from run boundaries alone (the fast
+ * route); otherwise they compare ids and positions (the general route).
+ * PR 3516 (Changes 3 and 4, Diagram) routes matching metadata to the fast
+ * path and differing metadata (cross-attention, rotated ring steps) to the
+ * general one.  The check runs on the device per batch row, and both routes
+ * give bitwise identical results.
+ *
+ * Layout.  Token-major BSHD: element (b, s, h, d) of a tensor lives at
+ * base + b*stride.batch + s*stride.token + h*stride.head + d (strides in
+ * elements, the head-dim axis contiguous).  dQ, dK, dV use the strides of
+ * Q, K, V; dO uses the strides of O (the output gradient must share the
+ * saved output's layout, the one-GPU form of the sharding alignment in
+ * PR 3516, Changes 1).  LSE is [B, Hq, Sq] fp32, contiguous.  Segment
+ * metadata are int32 [B, S], contiguous.
+ *
+ * Memory and streams.  Every pointer argument except route_out is device
+ * memory owned by the caller; the library allocates nothing and keeps no
+ * state besides a thread-local error string.  All work is enqueued on the
+ * given HIP stream (a hipStream_t passed as void*, NULL = default stream)
+ * and nothing synchronises.  The workspace must hold at least the size the
+ * matching *_workspace_size query returns for the same descriptor; its
+ * contents need no initialisation and are dead after the stream reaches the
+ * end of the call.  Calls that share a workspace must be ordered.
+ *
+ * Errors.  Arguments are validated on the host before any HIP call; on a
+ * failure nothing is launched and the status says why (attn_last_error()
+ * returns the text).  A failed launch returns ATTN_E_DEVICE.  No C++
+ * exception crosses this interface.
+ */
+#ifndef BPS_ATTN_H
+#define BPS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = 1,      /* inconsistent or missing arguments           */
+  ATTN_E_UNSUPPORTED = 2,  /* valid request outside what is built         */
+  ATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than required  */
+  ATTN_E_DEVICE = 4        /* a HIP call or kernel launch failed          */
+} attn_status;
+
+typedef enum {
+  ATTN_BF16 = 0,           /* bf16 tensors, fp32 accumulation             */
+  ATTN_FP32 = 1            /* fp32 tensors, fp32 accumulation             */
+} attn_dtype;
+
+/* attn_desc.flags */
+enum {
+  ATTN_FORCE_GENERAL = 1u << 0,     /* never take the fast route (tests, ring steps) */
+  ATTN_REVERSE_SCHEDULE = 1u << 1   /* visit workgroup tiles in reverse order (tests:
+                                       results must not depend on schedule) */
+};
+
+/* Route reported through route_out. */
+enum {
+  ATTN_ROUTE_DENSE = 0,    /* no metadata: plain or causal mask           */
+  ATTN_ROUTE_FAST = 1,     /* fast route requested; a batch row whose
+                              metadata fail the device check falls back to
+                              the general route                           */
+  ATTN_ROUTE_GENERAL = 2
+};
+
+typedef struct {
+  int64_t batch, token, head;       /* element strides; head dim contiguous */
+} attn_strides;
+
+typedef struct {
+  int32_t B, Sq, Skv;               /* batch rows, query / key tokens per row */
+  int32_t Hq, Hkv;                  /* query heads, key/value heads (Hq % Hkv == 0) */
+  int32_t Dqk, Dv;                  /* head dims: bf16 {64,128,192} x {64,128};
+                                       fp32 {64,128} x {64,128} */
+  int32_t dtype;                    /* attn_dtype */
+  int32_t causal;                   /* 0 or 1 */
+  float scale;                      /* softmax scale; 0 selects 1/sqrt(Dqk) */
+  uint32_t flags;                   /* ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE */
+  attn_strides q, k, v, o;          /* layouts of Q, K, V, O (and dQ, dK, dV, dO) */
+} attn_desc;
+
+typedef struct {
+  const int32_t* ids_q;    /* [B, Sq] device; required when the struct is given  */
+  const int32_t* pos_q;    /* [B, Sq] device; NULL: offset inside the run of ids  */
+  const int32_t* ids_kv;   /* [B, Skv] device; NULL: self-attention, KV metadata
+                              are Q's (needs Sq == Skv and pos_kv NULL)          */
+  const int32_t* pos_kv;   /* [B, Skv] device; NULL: derived from ids_kv          */
+} attn_segments;
+
+/* Workspace bytes needed by attn_fwd / attn_bwd for this descriptor and
+ * metadata (seg may be NULL).  Returns 0 for an invalid descriptor (the
+ * matching call then reports why). */
+size_t attn_fwd_workspace_size(const attn_desc* desc, const attn_segments* seg);
+size_t attn_bwd_workspace_size(const attn_desc* desc, const attn_segments* seg);
+
+/* Forward: O [B,Sq,Hq,Dv] (dtype of the inputs) and LSE [B,Hq,Sq] fp32.
+ * seg NULL means plain BSHD.  route_out (host, nullable) receives the route. */
+attn_status attn_fwd(const attn_desc* desc, const attn_segments* seg,
+                     const void* q, const void* k, const void* v,
+                     void* o, float* lse,
+                     void* workspace, size_t workspace_bytes,
+                     void* stream, int32_t* route_out);
+
+/* Backward: from Q, K, V, the saved O and LSE of attn_fwd, and dO, writes
+ * dQ, dK, dV (dtype of the inputs).  dK and dV are complete sums over each
+ * GQA group; every element is written exactly once by one workgroup, in a
+ * fixed order, so results are bitwise reproducible. */
+attn_status attn_bwd(const attn_desc* desc, const attn_segments* seg,
+                     const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     void* stream, int32_t* route_out);
+
+/* Test helper: writes the mask the kernels apply, mask_out[b][i][j] = 1 when
+ * query i may attend key j (uint8 [B,Sq,Skv], device), and, when route_rows
+ * is not NULL, the route each batch row takes (int32 [B], device: 0 dense,
+ * 1 fast, 2 general).  Uses the same device mask code and the same
+ * metadata preparation as attn_fwd; needs attn_fwd_workspace_size bytes. */
+attn_status attn_debug_mask(const attn_desc* desc, const attn_segments* seg,
+                            uint8_t* mask_out, int32_t* route_rows,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPS_ATTN_H */

@@ -1,0 +1,153 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host validation rejects bad arguments before any HIP call
+(so these run without a GPU; nothing here launches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bwd_packed_segments_amd as bps
+from bwd_packed_segments_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bps_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.library_path()),
+                                reason="libbps_attn.so not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = B.lib()
+    declared = header_functions()
+    assert set(declared) == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_error_string():
+    L = B.lib()
+    assert b"gfx950" in L.attn_version()
+    assert isinstance(L.attn_last_error(), bytes)
+
+
+def good(**kw):
+    base = dict(B=2, Sq=300, Skv=300, Hq=4, Hkv=2, Dqk=128, Dv=128, causal=True)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+def test_workspace_sizes():
+    d = good()
+    assert B.fwd_workspace_size(d) == 0                       # no metadata: no workspace
+    assert B.bwd_workspace_size(d) >= 2 * 2 * 4 * 300 * 4      # delta + lse2
+    seg = B.attn_segments(0x1000, None, None, None)
+    assert B.fwd_workspace_size(d, seg) > 0
+    seg2 = B.attn_segments(0x1000, 0x2000, 0x3000, 0x4000)
+    assert B.fwd_workspace_size(d, seg2) > B.fwd_workspace_size(d, B.attn_segments(0x1000, 0x2000, None, None))
+    bad = good(Hq=3)
+    assert B.fwd_workspace_size(bad) == 0
+
+
+CASES = [
+    ("hq_not_multiple", dict(Hq=6, Hkv=4), None, B.ATTN_E_INVALID, "multiple"),
+    ("zero_heads", dict(Hkv=0), None, B.ATTN_E_INVALID, "positive"),
+    ("neg_len", dict(Sq=-1), None, B.ATTN_E_INVALID, "positive"),
+    ("dims", dict(Dqk=96), None, B.ATTN_E_UNSUPPORTED, "head dims"),
+    ("dims_fp32_192", dict(Dqk=192, dtype=B.ATTN_FP32), None, B.ATTN_E_UNSUPPORTED, "head dims"),
+    ("dtype", dict(dtype=7), None, B.ATTN_E_INVALID, "dtype"),
+    ("causal_value", dict(causal=True), None, None, None),
+    ("causal_unequal_nometa", dict(Skv=200), None, B.ATTN_E_UNSUPPORTED, "Sq == Skv"),
+    ("scale_nan", dict(scale=float("nan")), None, B.ATTN_E_INVALID, "scale"),
+    ("scale_neg", dict(scale=-1.0), None, B.ATTN_E_INVALID, "scale"),
+    ("flags", dict(flags=1 << 7), None, B.ATTN_E_INVALID, "flag"),
+    ("stride_align", dict(q=(300 * 4 * 128, 4 * 128, 124)), None, B.ATTN_E_UNSUPPORTED, "multiples"),
+    ("stride_neg", dict(k=(-1, 256, 128)), None, B.ATTN_E_INVALID, "non-negative"),
+    ("meta_no_ids", dict(), B.attn_segments(None, 0x1000, None, None), B.ATTN_E_INVALID, "ids_q"),
+    ("meta_pos_kv_alone", dict(), B.attn_segments(0x1000, None, None, 0x2000), B.ATTN_E_INVALID, "pairs"),
+    ("meta_self_unequal", dict(Skv=200), B.attn_segments(0x1000, None, None, None), B.ATTN_E_INVALID, "Sq == Skv"),
+]
+
+
+@pytest.mark.parametrize("name,kw,seg,status,msg", CASES, ids=[c[0] for c in CASES])
+def test_validation(name, kw, seg, status, msg):
+    d = good(**kw)
+    if status is None:
+        d.causal = 2
+        status, msg = B.ATTN_E_INVALID, "causal"
+    st, text = B.validate_fwd(d, seg)
+    assert st == status, text
+    assert msg in text
+    st, text = B.validate_bwd(d, seg)
+    assert st == status, text
+
+
+def test_null_pointers_rejected():
+    st, text = B.validate_fwd(good(), q=None)
+    assert st == B.ATTN_E_INVALID and "NULL" in text
+    st, text = B.validate_bwd(good(), dq=None)
+    assert st == B.ATTN_E_INVALID and "NULL" in text
+
+
+def test_misaligned_pointer_rejected():
+    st, text = B.validate_fwd(good(), q=(1 << 12) + 2)
+    assert st == B.ATTN_E_UNSUPPORTED and "aligned" in text
+
+
+def test_workspace_checks():
+    seg = B.attn_segments(0x1000, None, None, None)
+    d = good()
+    need = B.fwd_workspace_size(d, seg)
+    st, text = B.validate_fwd(d, seg, ws=1 << 20, ws_bytes=need - 1)
+    assert st == B.ATTN_E_WORKSPACE and "smaller" in text
+    st, text = B.validate_fwd(d, seg, ws=None, ws_bytes=need)
+    assert st == B.ATTN_E_WORKSPACE and "NULL" in text
+    st, text = B.validate_fwd(d, seg, ws=(1 << 20) + 64, ws_bytes=need)
+    assert st == B.ATTN_E_WORKSPACE and "aligned" in text
+    st, text = B.validate_bwd(d, seg, ws=1 << 20, ws_bytes=B.bwd_workspace_size(d, seg) - 1)
+    assert st == B.ATTN_E_WORKSPACE
+
+
+def test_null_desc():
+    L = B.lib()
+    st = L.attn_fwd(None, None, 1, 1, 1, 1, 1, None, 0, None, None)
+    assert st == B.ATTN_E_INVALID
+    assert L.attn_fwd_workspace_size(None, None) == 0
+
+
+def test_error_is_thread_local():
+    import threading
+    B.validate_fwd(good(Hq=6, Hkv=4))
+    seen = {}
+
+    def other():
+        seen["msg"] = B.lib().attn_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == b""
+    assert b"multiple" in B.lib().attn_last_error()
+
+
+def test_product_path_has_no_oracle_import():
+    """The binding and the package never import the oracle (test-only)."""
+    pkg = os.path.join(ROOT, "bwd_packed_segments_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py") and fn != "inputs.py":
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src.replace("oracle)", ""), fn
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setenv("BPS_ATTN_LIB", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        B.lib()
+    monkeypatch.setattr(B, "_lib", None)

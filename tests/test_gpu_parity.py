@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs, element by element.
+
+Small shapes span several tiles and a ragged tail so the oracle finishes in
+seconds; the full benchmark shapes are compared on a sample of heads the
+oracle computes exactly (for dK/dV: whole GQA groups)."""
+
+import numpy as np
+import pytest
+
+from bwd_packed_segments_amd import inputs
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = [0, 1, 2]
+
+
+def _parity(case, heads=None, flags=0):
+    print(f"[parity] {case['workload']} seed={case['seed']} flags={flags}", flush=True)
+    gpu = G.numpy_out(G.run_gpu(case, flags=flags))
+    ref = G.run_oracle(case, heads=heads)
+    return G.check_all(case, gpu, ref), gpu, ref
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_tiny_fp32(seed):
+    case = inputs.make_case("tiny_fp32", seed)
+    _parity(case)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("causal", [True, False])
+def test_bshd_small(seed, causal):
+    case = G.small_case("bshd_causal_2k", seed, B=2, S=300, Hq=4, Hkv=4, causal=causal)
+    _parity(case)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_thd_packed_small(seed):
+    case = G.small_case("thd_packed_8k", seed, B=2, S=700, Hq=4, Hkv=4, seg_lo=16, seg_hi=300)
+    stats, gpu, _ = _parity(case)
+    assert gpu["route"] == "fast"
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_gqa_causal_small(seed):
+    case = G.small_case("gqa_causal_8k", seed, S=520, Hq=8, Hkv=2)
+    _parity(case)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_thd_cross_small(seed):
+    case = G.small_case("thd_cross_ring_4k", seed, Sq=600, Skv=700, Hq=4, Hkv=2, seg_lo=32, seg_hi=256)
+    stats, gpu, _ = _parity(case)
+    assert gpu["route"] == "general"
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_thd_cross_causal_positions(seed):
+    """Cross metadata with a causal mask over positions (general route)."""
+    case = G.small_case("thd_cross_ring_4k", seed, Sq=500, Skv=500, Hq=4, Hkv=1, seg_lo=32, seg_hi=200,
+                        causal=True)
+    _parity(case)
+
+
+@pytest.mark.parametrize("dqk,dv", [(64, 64), (64, 128), (128, 64), (192, 64), (192, 128)])
+def test_head_dims_bf16(dqk, dv):
+    case = G.small_case("gqa_causal_8k", 3, S=200, Hq=4, Hkv=2, Dqk=dqk, Dv=dv)
+    _parity(case)
+
+
+@pytest.mark.parametrize("dqk,dv,causal", [(128, 128, True), (64, 128, False), (128, 64, True)])
+def test_head_dims_fp32(dqk, dv, causal):
+    case = G.small_case("tiny_fp32", 4, S=190, Hq=2, Hkv=1, Dqk=dqk, Dv=dv, causal=causal)
+    _parity(case)
+
+
+def test_odd_lengths_cross():
+    """Non-divisible lengths (1350 queries, 1777 keys), GQA."""
+    case = G.small_case("thd_cross_ring_4k", 5, Sq=1350, Skv=1777, Hq=4, Hkv=2, Dqk=128, seg_lo=64, seg_hi=700)
+    _parity(case)
+
+
+def test_odd_lengths_dense():
+    case = G.small_case("bshd_causal_2k", 6, B=1, Sq=1350, Skv=1777, Hq=2, Hkv=1, causal=False)
+    _parity(case)
+
+
+def test_packed_pos_derived_on_device():
+    """pos omitted: derived on the device from ids."""
+    case = G.small_case("thd_packed_8k", 7, B=2, S=400, Hq=2, Hkv=2, seg_lo=16, seg_hi=200)
+    seg = dict(case["segments"])
+    seg["pos_q"] = None
+    case["segments"] = seg
+    _parity(case)
+
+
+def test_unsorted_ids_take_general_route():
+    """Ids that reappear in two runs are not fast-route eligible; results
+    still match the oracle."""
+    case = G.small_case("thd_packed_8k", 8, B=1, S=256, Hq=2, Hkv=2, seg_lo=16, seg_hi=64)
+    ids = np.array(case["segments"]["ids_q"])
+    ids[0, 200:230] = 1                     # id 1 again, far from its first run
+    from oracle import derive_pos
+    case["segments"] = {"ids_q": ids, "pos_q": derive_pos(ids)}
+    stats, gpu, _ = _parity(case)
+
+
+def test_strided_packed_qkv():
+    """Q, K, V as views into one packed [B, S, 3, H, D] buffer (element strides)."""
+    import torch
+    case = G.small_case("bshd_causal_2k", 9, B=2, S=260, Hq=4, Hkv=4)
+    qkv = np.stack([case["q"], case["k"], case["v"]], axis=2)           # [B, S, 3, H, D]
+    t = G.to_dev(qkv, "bf16")
+    tensors = {"q": t[:, :, 0], "k": t[:, :, 1], "v": t[:, :, 2], "do": G.to_dev(case["do"], "bf16")}
+    print("[parity] strided packed qkv", flush=True)
+    gpu = G.numpy_out(G.run_gpu(case, tensors=tensors))
+    ref = G.run_oracle(case)
+    G.check_all(case, gpu, ref)
+    assert tensors["q"].stride()[1] == 3 * 4 * 128
+
+
+def test_empty_kv_and_empty_q():
+    import torch
+    import bwd_packed_segments_amd as bps
+    print("[edge] empty kv", flush=True)
+    q = torch.randn(1, 70, 2, 64, device="cuda").to(torch.bfloat16)
+    k = torch.zeros(1, 0, 1, 64, device="cuda", dtype=torch.bfloat16)
+    v = torch.zeros(1, 0, 1, 64, device="cuda", dtype=torch.bfloat16)
+    o, lse = bps.attn_fwd(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    do = torch.randn_like(o)
+    dq, dk, dv = bps.attn_bwd(q, k, v, o, lse, do, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and dk.numel() == 0
+    print("[edge] empty q", flush=True)
+    q0 = torch.zeros(1, 0, 2, 64, device="cuda", dtype=torch.bfloat16)
+    k1 = torch.randn(1, 9, 1, 64, device="cuda").to(torch.bfloat16)
+    o0, lse0 = bps.attn_fwd(q0, k1, k1, causal=False)
+    dq0, dk0, dv0 = bps.attn_bwd(q0, k1, k1, o0, lse0, o0, causal=False)
+    torch.cuda.synchronize()
+    assert o0.numel() == 0 and torch.all(dk0 == 0) and torch.all(dv0 == 0)
+
+
+def test_all_padding_row():
+    """A batch row made only of padding: O = 0, LSE = -inf, all gradients 0."""
+    case = G.small_case("thd_packed_8k", 10, B=2, S=300, Hq=2, Hkv=2, seg_lo=16, seg_hi=100)
+    ids = np.array(case["segments"]["ids_q"])
+    ids[1] = 0
+    case["segments"] = {"ids_q": ids, "pos_q": np.zeros_like(ids)}
+    stats, gpu, _ = _parity(case)
+    assert np.all(gpu["O"][1] == 0) and np.all(np.isneginf(gpu["LSE"][1]))
+    for k in ("dQ", "dK", "dV"):
+        assert np.all(gpu[k][1] == 0)
+
+
+def test_single_token():
+    case = G.small_case("bshd_causal_2k", 11, B=1, S=1, Hq=2, Hkv=1)
+    _parity(case)
+
+
+# ------------------------------------------------------------ full sizes
+
+FULL = [
+    ("bshd_causal_2k", [0, 15]),
+    ("thd_packed_8k", [0, 31]),
+    ("gqa_causal_8k", list(range(8))),      # whole group of KV head 0
+    ("thd_cross_ring_4k", list(range(4))),  # whole group of KV head 0
+]
+
+
+@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled_heads(name, heads):
+    """The benchmark workloads at full size, in the launch configuration the
+    bench times; the oracle computes a sample of heads exactly."""
+    case = inputs.make_case(name, 0)
+    _parity(case, heads=heads)
