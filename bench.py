@@ -1,0 +1,281 @@
+"""Benchmark: fused attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is the whole hot path over one batch of synthetic input already in
+HBM: forward (O, LSE), backward preparation (segment metadata when present,
+Delta), dK/dV and dQ.  Prints one JSON line:
+
+  value      algorithmic fwd+bwd TFLOP/s, F = 2 n (4 Dqk + 3 Dv) with n the
+             number of allowed (query, key) pairs over batch rows and query
+             heads (masked pairs are not counted)
+  roofline   the slowest kernel of the step against the bf16 dense MFMA peak
+             (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk); its time is
+             the average of HIP events recorded around its launch on the
+             stream it runs on
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+             (a few query heads), timed on the host cores
+
+The workload is the 8K causal GQA configuration unless --workload says
+otherwise; the others are parity-test cases.  Only one GPU is used.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from bwd_packed_segments_amd import inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_TFLOPS = 157.3
+METRIC = "fwd+bwd attention TFLOP/s (bf16) and % of MI355X MFMA peak, 1 GPU"
+DEFAULT_WORKLOAD = "gqa_causal_8k"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["bps_common.hpp", "attn_kernels.hpp"]
+
+
+# ------------------------------------------------------------------ counting
+
+def allowed_pairs(w, segments) -> int:
+    """Number of allowed (query, key) pairs summed over batch rows and query
+    heads, counted from the metadata directly."""
+    if segments is None:
+        if w.causal:
+            per_row = w.Sq * (w.Sq + 1) // 2
+        else:
+            per_row = w.Sq * w.Skv
+        return w.B * w.Hq * per_row
+    ids_q = np.asarray(segments["ids_q"])
+    pos_q = segments.get("pos_q")
+    ids_kv = segments.get("ids_kv")
+    if ids_kv is None:
+        ids_kv, pos_kv = ids_q, pos_q
+    else:
+        ids_kv = np.asarray(ids_kv)
+        pos_kv = segments.get("pos_kv")
+    total = 0
+    for b in range(w.B):
+        for s in np.unique(ids_q[b]):
+            if s == 0:
+                continue
+            qi = np.nonzero(ids_q[b] == s)[0]
+            kj = np.nonzero(ids_kv[b] == s)[0]
+            if not w.causal:
+                total += qi.size * kj.size
+            else:
+                kp = np.sort(np.asarray(pos_kv)[b, kj])
+                qp = np.asarray(pos_q)[b, qi]
+                total += int(np.searchsorted(kp, qp, side="right").sum())
+    return total * w.Hq
+
+
+def flops(w, n):
+    return {
+        "fwd": 2.0 * n * (w.Dqk + w.Dv),
+        "bwd": 2.0 * n * (3 * w.Dqk + 2 * w.Dv),
+        # per kernel: the contractions each one must do over allowed pairs
+        "k_fwd": 2.0 * n * (w.Dqk + w.Dv),
+        "k_dkdv": 2.0 * n * (2 * w.Dqk + 2 * w.Dv),
+        "k_dq": 2.0 * n * (2 * w.Dqk + w.Dv),
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bwd_packed_segments_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(f"{kernel}:{workload}")
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ GPU timing
+
+def run_gpu(w, steps, warmup, seed=0):
+    import torch
+    import bwd_packed_segments_amd as bps
+
+    case = inputs.make_case(w, seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = {k: torch.from_numpy(case[k]).to("cuda").to(dt) for k in ("q", "k", "v", "do")}
+    seg = None
+    if case["segments"] is not None:
+        sg = case["segments"]
+
+        def t(x):
+            return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
+        seg = bps.Segments(t(sg["ids_q"]), t(sg.get("pos_q")), t(sg.get("ids_kv")), t(sg.get("pos_kv")))
+    fwd = bps.FwdPlan(dev["q"], dev["k"], dev["v"], causal=w.causal, segments=seg)
+    bwd = bps.BwdPlan(dev["q"], dev["k"], dev["v"], fwd.o, fwd.lse, dev["do"], causal=w.causal, segments=seg)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fwd.run()
+        if ev is not None:
+            ev[1].record(stream)
+        bwd.run(bps.ATTN_BWD_PREPARE)
+        if ev is not None:
+            ev[2].record(stream)
+        bwd.run(bps.ATTN_BWD_DKDV)
+        if ev is not None:
+            ev[3].record(stream)
+        bwd.run(bps.ATTN_BWD_DQ)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phases = {"fwd": [], "prepare": [], "dkdv": [], "dq": [], "step": []}
+    for ev in events:
+        phases["fwd"].append(ev[0].elapsed_time(ev[1]))
+        phases["prepare"].append(ev[1].elapsed_time(ev[2]))
+        phases["dkdv"].append(ev[2].elapsed_time(ev[3]))
+        phases["dq"].append(ev[3].elapsed_time(ev[4]))
+        phases["step"].append(ev[0].elapsed_time(ev[4]))
+    avg = {k: float(np.mean(v)) for k, v in phases.items()}
+    med = {k: float(np.median(v)) for k, v in phases.items()}
+    return case, wall, avg, med, fwd.route
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(w, case, n_alg_per_head_flops, budget_s=15.0):
+    """The fp64 oracle (test infrastructure) on a sample of query heads of
+    the same inputs, forward + backward, until about budget_s seconds."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    heads = []
+    t_total = 0.0
+    h = 0
+    while h < w.Hq and (t_total < budget_s or not heads):
+        t0 = time.perf_counter()
+        oracle.forward(case["q"], case["k"], case["v"], causal=w.causal, segments=case["segments"], heads=[h])
+        oracle.backward(case["q"], case["k"], case["v"], case["do"], causal=w.causal, segments=case["segments"],
+                        heads=[h])
+        t_total += time.perf_counter() - t0
+        heads.append(h)
+        h += 1
+        if t_total / len(heads) * (len(heads) + 1) > 2 * budget_s:
+            break
+    value = n_alg_per_head_flops * len(heads) / t_total / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: forward+backward of {len(heads)} of {w.Hq} query heads "
+                      f"(batch rows all), {t_total:.1f} s, fp64 NumPy",
+            "seconds": t_total}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no multi-GPU path. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w = inputs.WORKLOADS[args.workload]
+    t_setup = time.perf_counter()
+    case, wall, avg, med, route = run_gpu(w, args.steps, args.warmup)
+    n = allowed_pairs(w, case["segments"])
+    F = flops(w, n)
+    f_step = F["fwd"] + F["bwd"]
+    ms_per_step = wall / args.steps * 1e3
+    value = f_step / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    kernels = {"attn_fwd": (avg["fwd"], F["k_fwd"]), "attn_bwd_dkdv": (avg["dkdv"], F["k_dkdv"]),
+               "attn_bwd_dq": (avg["dq"], F["k_dq"])}
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    ms_dom, f_dom = kernels[dom]
+    achieved = f_dom / (ms_dom * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, w.name), "kernel": dom,
+                "avg_ms": round(ms_dom, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1) tensors, seed 0)",
+        "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "metadata": w.meta, "route": route,
+                   "allowed_pairs": n, "flop_per_step": f_step},
+        "pct_peak": round(100.0 * value / peak, 2),
+        "phase_ms": {k: round(v, 4) for k, v in avg.items()},
+        "phase_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, case, f_step / w.Hq, args.cpu_seconds)
+        cb.pop("seconds", None)
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(f"# {w.name}: {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak), {ms_per_step:.3f} ms/step; "
+          f"phases {json.dumps(out['phase_ms'])}; setup+run {time.perf_counter() - t_setup:.1f}s", file=sys.stderr)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

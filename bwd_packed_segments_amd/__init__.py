@@ -11,7 +11,13 @@ call does, and it raises if the library is missing.
 from .binding import (  # noqa: F401
     ATTN_FORCE_GENERAL,
     ATTN_REVERSE_SCHEDULE,
+    ATTN_BWD_ALL,
+    ATTN_BWD_DKDV,
+    ATTN_BWD_DQ,
+    ATTN_BWD_PREPARE,
     AttnError,
+    BwdPlan,
+    FwdPlan,
     Segments,
     attn_bwd,
     attn_debug_mask,

@@ -27,8 +27,9 @@ STATUS_NAMES = {
 }
 
 # Every symbol the header declares (the CPU tests check the library exports them).
-EXPORTS = ("attn_fwd_workspace_size", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
+EXPORTS = ("attn_fwd_workspace_size", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_phase",
            "attn_debug_mask", "attn_last_error", "attn_version")
+ATTN_BWD_PREPARE, ATTN_BWD_DKDV, ATTN_BWD_DQ, ATTN_BWD_ALL = 1, 2, 4, 7
 
 
 class AttnError(RuntimeError):
@@ -87,6 +88,8 @@ def lib():
         L.attn_fwd.restype = ctypes.c_int
         L.attn_bwd.argtypes = [dp, sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i32p]
         L.attn_bwd.restype = ctypes.c_int
+        L.attn_bwd_phase.argtypes = [ctypes.c_int32, dp, sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i32p]
+        L.attn_bwd_phase.restype = ctypes.c_int
         L.attn_debug_mask.argtypes = [dp, sp, vp, vp, vp, sz, vp]
         L.attn_debug_mask.restype = ctypes.c_int
         L.attn_last_error.argtypes = []
@@ -244,6 +247,66 @@ def attn_bwd(q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segment
                       lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                       ws.data_ptr(), ws.numel(), _stream(q.device), None))
     return dq, dk, dv
+
+
+class FwdPlan:
+    """A forward for fixed tensors with its outputs and workspace allocated
+    once, so that repeated calls allocate nothing."""
+
+    def __init__(self, q, k, v, *, causal=False, scale=None, segments: Segments | None = None, flags=0):
+        import torch
+        _require_device(q, k, v)
+        B, Sq, Hq, _ = q.shape
+        self.t = (q, k, v)
+        self.o = torch.empty((B, Sq, Hq, v.shape[3]), dtype=q.dtype, device=q.device)
+        self.lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+        self.desc = _desc_for(q, k, v, _strides(self.o), causal, scale, flags)
+        self.cs, self.csp = _seg_ptr(segments)
+        self.segments = segments
+        self.ws = _workspace(lib().attn_fwd_workspace_size(ctypes.byref(self.desc), self.csp), q.device)
+        self.route = None
+
+    def run(self, stream=None):
+        q, k, v = self.t
+        st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(q.device)
+        route = ctypes.c_int32(-1)
+        _check(lib().attn_fwd(ctypes.byref(self.desc), self.csp, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              self.o.data_ptr(), self.lse.data_ptr(), self.ws.data_ptr(), self.ws.numel(), st,
+                              ctypes.byref(route)))
+        self.route = ROUTE_NAMES[route.value]
+        return self.o, self.lse
+
+
+class BwdPlan:
+    """A backward prepared once for fixed tensors, whose phases can be
+    launched separately (prepare, then dK/dV and dQ in either order or on
+    two streams).  Holds the outputs and the workspace."""
+
+    def __init__(self, q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segments | None = None,
+                 flags=0):
+        import torch
+        _require_device(q, k, v, o, lse, do)
+        if do.stride() != o.stride() or do.shape != o.shape:
+            raise ValueError("dO must have the shape and strides of O")
+        self.t = (q, k, v, o, lse, do)
+        self.dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        self.dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+        self.dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+        self.desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
+        self.cs, self.csp = _seg_ptr(segments)
+        self.segments = segments
+        L = lib()
+        self.ws = _workspace(L.attn_bwd_workspace_size(ctypes.byref(self.desc), self.csp), q.device)
+
+    def run(self, phases=ATTN_BWD_ALL, stream=None):
+        import torch
+        q, k, v, o, lse, do = self.t
+        st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(q.device)
+        _check(lib().attn_bwd_phase(phases, ctypes.byref(self.desc), self.csp, q.data_ptr(), k.data_ptr(),
+                                    v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), self.dq.data_ptr(),
+                                    self.dk.data_ptr(), self.dv.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+                                    st, None))
+        return self.dq, self.dk, self.dv
 
 
 def attn_debug_mask(*, B, Sq, Skv, causal=False, segments: Segments | None = None, flags=0, device="cuda"):

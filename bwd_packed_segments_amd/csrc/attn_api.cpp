@@ -141,7 +141,7 @@ bps::AttnShape shape_of(const attn_desc* d, const Plan& p) {
 
 // Launches the metadata preparation and fills the kernels' view of it.
 attn_status prepare_segments(const attn_desc* d, const attn_segments* seg, const Plan& p, char* ws,
-                             hipStream_t st, bps::SegView* view) {
+                             hipStream_t st, bps::SegView* view, bool launch = true) {
   *view = bps::SegView{};
   if (!p.meta) return ATTN_OK;
   bps::SegMetaArgs m{};
@@ -191,48 +191,52 @@ attn_status prepare_segments(const attn_desc* d, const attn_segments* seg, const
     view->nch_kv = view->nch_q;
   }
   view->route = m.route;
-  if (d->B == 0 || (d->Sq == 0 && d->Skv == 0)) return ATTN_OK;
+  if (!launch || d->B == 0 || (d->Sq == 0 && d->Skv == 0)) return ATTN_OK;
   hipError_t e = bps::launch_seg_meta(m, st);
   if (e != hipSuccess) return fail(ATTN_E_DEVICE, "segment metadata kernel: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
 
-template <typename T>
-hipError_t dispatch_fwd(int dqk, int dv, const bps::FwdArgs& a, hipStream_t st) {
-  if (dqk == 64 && dv == 64) return bps::launch_fwd<T, 64, 64>(a, st);
-  if (dqk == 64 && dv == 128) return bps::launch_fwd<T, 64, 128>(a, st);
-  if (dqk == 128 && dv == 64) return bps::launch_fwd<T, 128, 64>(a, st);
-  if (dqk == 128 && dv == 128) return bps::launch_fwd<T, 128, 128>(a, st);
+// Head-dim pairs built for each element type (must match build.py).
+#define BPS_BF16_DIMS(X) X(64, 64) X(64, 128) X(128, 64) X(128, 128) X(192, 64) X(192, 128)
+#define BPS_FP32_DIMS(X) X(64, 64) X(64, 128) X(128, 64) X(128, 128)
+
+template <typename T, int DQK, int DV>
+hipError_t run_bwd_phases(int phases, const bps::BwdArgs& a, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if ((phases & ATTN_BWD_PREPARE) && (e = bps::launch_bwd_delta<T, DQK, DV>(a, st)) != hipSuccess) return e;
+  if ((phases & ATTN_BWD_DKDV) && (e = bps::launch_bwd_dkdv<T, DQK, DV>(a, st)) != hipSuccess) return e;
+  if ((phases & ATTN_BWD_DQ) && (e = bps::launch_bwd_dq<T, DQK, DV>(a, st)) != hipSuccess) return e;
+  return e;
+}
+
+hipError_t dispatch_fwd(int dtype, int dqk, int dv, const bps::FwdArgs& a, hipStream_t st) {
+#define BPS_FWD_BF16(DQK, DV) \
+  if (dqk == DQK && dv == DV) return bps::launch_fwd<bps::bf16, DQK, DV>(a, st);
+#define BPS_FWD_FP32(DQK, DV) \
+  if (dqk == DQK && dv == DV) return bps::launch_fwd<float, DQK, DV>(a, st);
+  if (dtype == ATTN_BF16) {
+    BPS_BF16_DIMS(BPS_FWD_BF16)
+  } else {
+    BPS_FP32_DIMS(BPS_FWD_FP32)
+  }
+#undef BPS_FWD_BF16
+#undef BPS_FWD_FP32
   return hipErrorInvalidValue;
 }
-template <typename T>
-hipError_t dispatch_bwd(int dqk, int dv, const bps::BwdArgs& a, hipStream_t st) {
-  if (dqk == 64 && dv == 64) return bps::launch_bwd<T, 64, 64>(a, st);
-  if (dqk == 64 && dv == 128) return bps::launch_bwd<T, 64, 128>(a, st);
-  if (dqk == 128 && dv == 64) return bps::launch_bwd<T, 128, 64>(a, st);
-  if (dqk == 128 && dv == 128) return bps::launch_bwd<T, 128, 128>(a, st);
-  return hipErrorInvalidValue;
-}
-template <>
-hipError_t dispatch_fwd<bps::bf16>(int dqk, int dv, const bps::FwdArgs& a, hipStream_t st) {
-  using T = bps::bf16;
-  if (dqk == 64 && dv == 64) return bps::launch_fwd<T, 64, 64>(a, st);
-  if (dqk == 64 && dv == 128) return bps::launch_fwd<T, 64, 128>(a, st);
-  if (dqk == 128 && dv == 64) return bps::launch_fwd<T, 128, 64>(a, st);
-  if (dqk == 128 && dv == 128) return bps::launch_fwd<T, 128, 128>(a, st);
-  if (dqk == 192 && dv == 64) return bps::launch_fwd<T, 192, 64>(a, st);
-  if (dqk == 192 && dv == 128) return bps::launch_fwd<T, 192, 128>(a, st);
-  return hipErrorInvalidValue;
-}
-template <>
-hipError_t dispatch_bwd<bps::bf16>(int dqk, int dv, const bps::BwdArgs& a, hipStream_t st) {
-  using T = bps::bf16;
-  if (dqk == 64 && dv == 64) return bps::launch_bwd<T, 64, 64>(a, st);
-  if (dqk == 64 && dv == 128) return bps::launch_bwd<T, 64, 128>(a, st);
-  if (dqk == 128 && dv == 64) return bps::launch_bwd<T, 128, 64>(a, st);
-  if (dqk == 128 && dv == 128) return bps::launch_bwd<T, 128, 128>(a, st);
-  if (dqk == 192 && dv == 64) return bps::launch_bwd<T, 192, 64>(a, st);
-  if (dqk == 192 && dv == 128) return bps::launch_bwd<T, 192, 128>(a, st);
+
+hipError_t dispatch_bwd(int phases, int dtype, int dqk, int dv, const bps::BwdArgs& a, hipStream_t st) {
+#define BPS_BWD_BF16(DQK, DV) \
+  if (dqk == DQK && dv == DV) return run_bwd_phases<bps::bf16, DQK, DV>(phases, a, st);
+#define BPS_BWD_FP32(DQK, DV) \
+  if (dqk == DQK && dv == DV) return run_bwd_phases<float, DQK, DV>(phases, a, st);
+  if (dtype == ATTN_BF16) {
+    BPS_BF16_DIMS(BPS_BWD_BF16)
+  } else {
+    BPS_FP32_DIMS(BPS_BWD_FP32)
+  }
+#undef BPS_BWD_BF16
+#undef BPS_BWD_FP32
   return hipErrorInvalidValue;
 }
 
@@ -292,8 +296,7 @@ attn_status attn_fwd(const attn_desc* d, const attn_segments* seg, const void* q
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
     if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg)) != ATTN_OK) return st;
-    hipError_t e = d->dtype == ATTN_BF16 ? dispatch_fwd<bps::bf16>(d->Dqk, d->Dv, a, hs)
-                                         : dispatch_fwd<float>(d->Dqk, d->Dv, a, hs);
+    hipError_t e = dispatch_fwd(d->dtype, d->Dqk, d->Dv, a, hs);
     if (e != hipSuccess) return fail(ATTN_E_DEVICE, "forward launch: %s", hipGetErrorString(e));
     return ATTN_OK;
   } catch (...) {
@@ -301,19 +304,25 @@ attn_status attn_fwd(const attn_desc* d, const attn_segments* seg, const void* q
   }
 }
 
-attn_status attn_bwd(const attn_desc* d, const attn_segments* seg, const void* q, const void* k, const void* v,
-                     const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                     void* workspace, size_t workspace_bytes, void* stream, int32_t* route_out) {
+attn_status attn_bwd_phase(int32_t phases, const attn_desc* d, const attn_segments* seg, const void* q,
+                           const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                           void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream,
+                           int32_t* route_out) {
   try {
+    if (phases <= 0 || (phases & ~ATTN_BWD_ALL))
+      return fail(ATTN_E_INVALID, "phases must be a nonzero combination of ATTN_BWD_* bits (got %d)", phases);
     Plan p;
     attn_status st = make_plan(d, seg, &p);
     if (st != ATTN_OK) return st;
     const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
-    if (need_nonnull(q, nq) || need_nonnull(o, nq) || need_nonnull(lse, nq) || need_nonnull(dout, nq) ||
-        need_nonnull(dq, nq))
-      return fail(ATTN_E_INVALID, "q, o, lse, dout and dq must not be NULL");
-    if (need_nonnull(k, nkv) || need_nonnull(v, nkv) || need_nonnull(dk, nkv) || need_nonnull(dv, nkv))
-      return fail(ATTN_E_INVALID, "k, v, dk and dv must not be NULL");
+    if (need_nonnull(dout, nq)) return fail(ATTN_E_INVALID, "dout must not be NULL");
+    if ((phases & ATTN_BWD_PREPARE) && (need_nonnull(o, nq) || need_nonnull(lse, nq)))
+      return fail(ATTN_E_INVALID, "o and lse must not be NULL");
+    if ((phases & (ATTN_BWD_DKDV | ATTN_BWD_DQ)) && (need_nonnull(q, nq) || need_nonnull(k, nkv) || need_nonnull(v, nkv)))
+      return fail(ATTN_E_INVALID, "q, k and v must not be NULL");
+    if ((phases & ATTN_BWD_DQ) && need_nonnull(dq, nq)) return fail(ATTN_E_INVALID, "dq must not be NULL");
+    if ((phases & ATTN_BWD_DKDV) && (need_nonnull(dk, nkv) || need_nonnull(dv, nkv)))
+      return fail(ATTN_E_INVALID, "dk and dv must not be NULL");
     if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
         (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)) ||
         (st = check_align("dout", dout, d->dtype)) || (st = check_align("dq", dq, d->dtype)) ||
@@ -330,14 +339,21 @@ attn_status attn_bwd(const attn_desc* d, const attn_segments* seg, const void* q
     a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
     a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_delta);
     a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_lse2);
-    if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg)) != ATTN_OK) return st;
-    hipError_t e = d->dtype == ATTN_BF16 ? dispatch_bwd<bps::bf16>(d->Dqk, d->Dv, a, hs)
-                                         : dispatch_bwd<float>(d->Dqk, d->Dv, a, hs);
+    const bool prep = (phases & ATTN_BWD_PREPARE) != 0;
+    if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg, prep)) != ATTN_OK) return st;
+    hipError_t e = dispatch_bwd(phases, d->dtype, d->Dqk, d->Dv, a, hs);
     if (e != hipSuccess) return fail(ATTN_E_DEVICE, "backward launch: %s", hipGetErrorString(e));
     return ATTN_OK;
   } catch (...) {
     return fail(ATTN_E_DEVICE, "unexpected host exception");
   }
+}
+
+attn_status attn_bwd(const attn_desc* d, const attn_segments* seg, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream, int32_t* route_out) {
+  return attn_bwd_phase(ATTN_BWD_ALL, d, seg, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                        stream, route_out);
 }
 
 attn_status attn_debug_mask(const attn_desc* d, const attn_segments* seg, uint8_t* mask_out, int32_t* route_rows,

@@ -10,5 +10,7 @@
 
 namespace bps {
 template hipError_t launch_fwd<INST_T, INST_DQK, INST_DV>(const FwdArgs&, hipStream_t);
-template hipError_t launch_bwd<INST_T, INST_DQK, INST_DV>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_delta<INST_T, INST_DQK, INST_DV>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dkdv<INST_T, INST_DQK, INST_DV>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dq<INST_T, INST_DQK, INST_DV>(const BwdArgs&, hipStream_t);
 }  // namespace bps

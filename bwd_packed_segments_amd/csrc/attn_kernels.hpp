@@ -920,33 +920,30 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
 }
 
 template <typename T, int DQK, int DV>
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st) {
   const size_t rows = (size_t)a.s.B * a.s.Sq * a.s.Hq;
-  if (rows > 0) {
-    const size_t blocks = (rows * 8 + 255) / 256;
-    hipLaunchKernelGGL((attn_bwd_delta_kernel<T, DV>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const int n_kt = (a.s.Skv + DkvCfg<T, DQK, DV>::BN - 1) / DkvCfg<T, DQK, DV>::BN;
-    const long long nblocks = (long long)a.s.B * a.s.Hkv * n_kt;
-    if (nblocks > 0) {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  {
-    const int n_qt = (a.s.Sq + DqCfg<T, DQK, DV>::BM - 1) / DqCfg<T, DQK, DV>::BM;
-    const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
-    if (nblocks > 0) {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  return hipSuccess;
+  if (rows == 0) return hipSuccess;
+  const size_t blocks = (rows * 8 + 255) / 256;
+  hipLaunchKernelGGL((attn_bwd_delta_kernel<T, DV>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DQK, int DV>
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
+  const int n_kt = (a.s.Skv + DkvCfg<T, DQK, DV>::BN - 1) / DkvCfg<T, DQK, DV>::BN;
+  const long long nblocks = (long long)a.s.B * a.s.Hkv * n_kt;
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DQK, int DV>
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
+  const int n_qt = (a.s.Sq + DqCfg<T, DQK, DV>::BM - 1) / DqCfg<T, DQK, DV>::BM;
+  const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace bps

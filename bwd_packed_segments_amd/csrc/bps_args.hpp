@@ -79,6 +79,10 @@ hipError_t launch_debug_mask(const MaskArgs& a, hipStream_t st);
 template <typename T, int DQK, int DV>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 template <typename T, int DQK, int DV>
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st);
+template <typename T, int DQK, int DV>
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st);
+template <typename T, int DQK, int DV>
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st);
 
 }  // namespace bps

@@ -152,6 +152,28 @@ attn_status attn_bwd(const attn_desc* desc, const attn_segments* seg,
                      void* workspace, size_t workspace_bytes,
                      void* stream, int32_t* route_out);
 
+/* Backward in phases, for callers that time or overlap them.  phases is a
+ * nonzero OR of the bits below; ATTN_BWD_ALL is attn_bwd.  PREPARE (segment
+ * metadata scan, Delta = rowsum(dO * O), LSE in base 2) fills the workspace
+ * that DKDV and DQ then read, so it must complete first on the stream (or be
+ * ordered before them with events) and the workspace must not change in
+ * between; DKDV and DQ are independent of each other and may run on two
+ * streams at once.  Arguments a phase does not use may be NULL (PREPARE uses
+ * o, lse, dout; DKDV uses q, k, v, dout, dk, dv; DQ uses q, k, v, dout, dq).
+ * Same descriptor, metadata and workspace size rules as attn_bwd. */
+enum {
+  ATTN_BWD_PREPARE = 1,
+  ATTN_BWD_DKDV = 2,
+  ATTN_BWD_DQ = 4,
+  ATTN_BWD_ALL = 7
+};
+attn_status attn_bwd_phase(int32_t phases, const attn_desc* desc, const attn_segments* seg,
+                           const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream, int32_t* route_out);
+
 /* Test helper: writes the mask the kernels apply, mask_out[b][i][j] = 1 when
  * query i may attend key j (uint8 [B,Sq,Skv], device), and, when route_rows
  * is not NULL, the route each batch row takes (int32 [B], device: 0 dense,

@@ -267,7 +267,7 @@ def backward(q, k, v, do, *, causal: bool, scale=None, segments=None, heads=None
     complete = [c for c in range(Hkv) if all(h in hs for h in range(c * g, c * g + g))]
     for b in range(B):
         mask = allowed_mask(b, Sq, Skv, causal, seg)
-        for c in complete:
+        for c in {kv_head_of(h, Hq, Hkv) for h in hs}:
             dK[b, :, c, :] = 0.0
             dV[b, :, c, :] = 0.0
         for h in hs:
@@ -278,10 +278,13 @@ def backward(q, k, v, do, *, causal: bool, scale=None, segments=None, heads=None
             delta = (P * dP).sum(axis=1)
             dS = P * (dP - delta[:, None])
             dQ[b, :, h, :] = scale * (dS @ kh)
-            if c in complete:
-                dK[b, :, c, :] += scale * (dS.T @ qh)
-                dV[b, :, c, :] += P.T @ doh
+            dK[b, :, c, :] += scale * (dS.T @ qh)
+            dV[b, :, c, :] += P.T @ doh
             O[b, :, h, :] = P @ vh
             LSE[b, h] = lse
             Delta[b, h] = delta
+    for c in range(Hkv):
+        if c not in complete:          # partial group sums are not results
+            dK[:, :, c, :] = np.nan
+            dV[:, :, c, :] = np.nan
     return {"dQ": dQ, "dK": dK, "dV": dV, "O": O, "LSE": LSE, "Delta": Delta}

@@ -17,7 +17,7 @@ def _mask_cases():
     rng = np.random.default_rng(0)
     out = []
     # packed self-attention, fast route
-    ids = np.array([[1] * 40 + [2] * 70 + [3] * 5 + [0] * 15, [5] * 60 + [9] * 70]], dtype=np.int32)
+    ids = np.array([[1] * 40 + [2] * 70 + [3] * 5 + [0] * 15, [5] * 60 + [9] * 70], dtype=np.int32)
     out.append(("packed_self", {"ids_q": ids, "pos_q": oracle.derive_pos(ids)}, 130, 130, True))
     out.append(("packed_self_nopos", {"ids_q": ids}, 130, 130, True))
     # unsorted ids / repeated id: general route
