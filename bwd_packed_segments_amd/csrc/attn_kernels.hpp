@@ -35,104 +35,9 @@
 #pragma once
 
 #include "bps_args.hpp"
+#include "lds_tile.hpp"
 
 namespace bps {
-
-// ------------------------------------------------------------ tile staging
-
-// Loads a [ROWS x D] tile (rows past nvalid read as zero) with consecutive
-// threads along a row, and stores it row-major into LDS.
-template <typename T, int ROWS, int D, int THREADS>
-struct RowTile {
-  using E = Elem<T>;
-  using F8 = typename E::F8;
-  static constexpr int UNITS = ROWS * (D / 8);
-  static constexpr int PER = UNITS / THREADS;
-  static_assert(UNITS % THREADS == 0, "tile must split evenly over the workgroup");
-  F8 r[PER];
-
-  __device__ void load(const T* base, int64_t row_stride, int nvalid, int tid) {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int u = tid + x * THREADS;
-      const int row = u / (D / 8);
-      const int c8 = u % (D / 8);
-      r[x] = row < nvalid ? E::load8(base + row * row_stride + c8 * 8) : E::zero8();
-    }
-  }
-  __device__ void store(T* lds, int stride, int tid) const {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int u = tid + x * THREADS;
-      const int row = u / (D / 8);
-      const int c8 = u % (D / 8);
-      *reinterpret_cast<F8*>(lds + row * stride + c8 * 8) = r[x];
-    }
-  }
-};
-
-// Loads a [ROWS x D] tile as row pairs so that it can also be stored
-// transposed: T[d][perm(row)], where perm swaps bits 2 and 3 of the row
-// index inside every group of 16 (the order the MFMA operands want).
-template <typename T, int ROWS, int D, int THREADS>
-struct PairTile {
-  using E = Elem<T>;
-  using F8 = typename E::F8;
-  using P2 = typename E::P2;
-  static constexpr int PAIRS = ROWS / 2;
-  static constexpr int UNITS = PAIRS * (D / 8);
-  static constexpr int PER = UNITS / THREADS;
-  static_assert(UNITS % THREADS == 0, "tile must split evenly over the workgroup");
-  static_assert(THREADS % PAIRS == 0, "row pairs must tile the workgroup");
-  F8 r0[PER], r1[PER];
-
-  __device__ static void unit(int u, int& pr, int& c8) {
-    pr = u % PAIRS;
-    c8 = u / PAIRS;
-  }
-  __device__ void load(const T* base, int64_t row_stride, int nvalid, int tid) {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      int pr, c8;
-      unit(tid + x * THREADS, pr, c8);
-      const int row = 2 * pr;
-      r0[x] = row < nvalid ? E::load8(base + row * row_stride + c8 * 8) : E::zero8();
-      r1[x] = row + 1 < nvalid ? E::load8(base + (row + 1) * row_stride + c8 * 8) : E::zero8();
-    }
-  }
-  __device__ void store_rows(T* lds, int stride, int tid) const {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      int pr, c8;
-      unit(tid + x * THREADS, pr, c8);
-      *reinterpret_cast<F8*>(lds + (2 * pr) * stride + c8 * 8) = r0[x];
-      *reinterpret_cast<F8*>(lds + (2 * pr + 1) * stride + c8 * 8) = r1[x];
-    }
-  }
-  __device__ void store_t(T* lds, int stride, int tid) const {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      int pr, c8;
-      unit(tid + x * THREADS, pr, c8);
-      const int row = 2 * pr;
-      const int col = (row & ~15) | perm16(row & 15);
-      T* dst = lds + (c8 * 8) * stride + col;
-      *reinterpret_cast<P2*>(dst + 0 * stride) = E::template pair<0>(r0[x], r1[x]);
-      *reinterpret_cast<P2*>(dst + 1 * stride) = E::template pair<1>(r0[x], r1[x]);
-      *reinterpret_cast<P2*>(dst + 2 * stride) = E::template pair<2>(r0[x], r1[x]);
-      *reinterpret_cast<P2*>(dst + 3 * stride) = E::template pair<3>(r0[x], r1[x]);
-      *reinterpret_cast<P2*>(dst + 4 * stride) = E::template pair<4>(r0[x], r1[x]);
-      *reinterpret_cast<P2*>(dst + 5 * stride) = E::template pair<5>(r0[x], r1[x]);
-      *reinterpret_cast<P2*>(dst + 6 * stride) = E::template pair<6>(r0[x], r1[x]);
-      *reinterpret_cast<P2*>(dst + 7 * stride) = E::template pair<7>(r0[x], r1[x]);
-    }
-  }
-};
-
-template <typename T>
-__device__ inline typename Elem<T>::F8 lds8(const T* p) {
-  return *reinterpret_cast<const typename Elem<T>::F8*>(p);
-}
 
 // Key tiles a query tile visits: [lo, hi) in tokens, per route.
 __device__ inline void kv_range(int route, bool causal, int Skv, int q0, int nq, const TileSum& qs, int& lo,
@@ -172,6 +77,31 @@ __device__ inline void q_range(int route, bool causal, int Sq, int k0, int nk, c
   if (hi < lo) hi = lo;
 }
 
+// LDS staging: two buffers when two workgroups with two buffers fit in the
+// 160 KB of a CU, otherwise one; two waves per SIMD when two workgroups fit.
+template <typename T, int STAGE>
+struct Staging {
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr int NBUF = (4 * STAGE <= LDS_MAX) ? 2 : 1;
+  static constexpr int WAVES_PER_EU = (sizeof(T) == 2 && 2 * NBUF * STAGE <= LDS_MAX) ? 2 : 1;
+};
+
+// Segment ids and positions of BN keys (general route) into LDS: direct
+// loads by waves 0 and 1 when the whole tile exists, else staged with zeros.
+template <int BN>
+__device__ inline void stage_kv_meta(const SegView& sv, int b, int Skv, int k0, int* kid, int tid, bool direct) {
+  static_assert(BN == 64, "one wave per metadata row");
+  const size_t row = (size_t)b * Skv + k0;
+  if (direct) {
+    if (tid < 64) __builtin_amdgcn_global_load_lds(sv.ids_kv + row + tid, (BPS_LDS void*)kid, 4, 0, 0);
+    else if (tid < 128) __builtin_amdgcn_global_load_lds(sv.pos_kv + row + (tid - 64), (BPS_LDS void*)(kid + BN), 4, 0, 0);
+  } else if (tid < 2 * BN) {
+    const int j = tid & (BN - 1);
+    const bool in = k0 + j < Skv;
+    kid[tid] = in ? (tid < BN ? sv.ids_kv[row + j] : sv.pos_kv[row + j]) : 0;
+  }
+}
+
 // ------------------------------------------------------------ forward
 
 template <typename T, int DQK, int DV>
@@ -179,24 +109,21 @@ struct FwdCfg {
   static constexpr int BM = 128;
   static constexpr int BN = 64;
   static constexpr int THREADS = 256;
-  static constexpr int NBUF = sizeof(T) == 2 ? 2 : 1;
-  static constexpr int KSTR = DQK + 8;
-  static constexpr int VTSTR = BN + 8;
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int VT_ELEMS = DV * VTSTR;
-  static constexpr int META_BYTES = 2 * BN * 4;
-  static constexpr int STAGE_BYTES = (K_ELEMS + VT_ELEMS) * (int)sizeof(T) + META_BYTES;
-  static constexpr int WAVES_PER_EU = (NBUF * STAGE_BYTES * 2 <= 160 * 1024) ? 2 : 1;
+  static constexpr int K_BYTES = BN * DQK * (int)sizeof(T);
+  static constexpr int V_BYTES = BN * DV * (int)sizeof(T);
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES + 2 * BN * 4;
+  static constexpr int NBUF = Staging<T, STAGE_BYTES>::NBUF;
+  static constexpr int WAVES_PER_EU = Staging<T, STAGE_BYTES>::WAVES_PER_EU;
 };
 
 template <typename T, int DQK, int DV>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, DQK, DV>::WAVES_PER_EU)))
     attn_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<T, DQK, DV>;
   using E = Elem<T>;
   using F8 = typename E::F8;
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __attribute__((aligned(16))) char smem[C::NBUF * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE_BYTES];
 
   const AttnShape& s = a.s;
   const bool causal = s.causal != 0;
@@ -231,6 +158,7 @@ __global__ void __launch_bounds__(256)
     qf[t] = qi < s.Sq ? E::load8(qp + qi * a.sq.t + 16 * t + 8 * hf) : E::zero8();
 
   const int route = s.has_meta ? a.seg.route[b] : kRouteDense;
+  const bool general = route == kRouteGeneral;
   const TokMeta qm = q_meta(route, a.seg, b, s.Sq, qi);
   TileSum qs{};
   const ChunkSum* sum_kv_row = nullptr;
@@ -256,39 +184,26 @@ __global__ void __launch_bounds__(256)
     cls = kTileSkip;
     return t_hi;
   };
-
-  RowTile<T, BN, DQK, 256> kreg;
-  PairTile<T, BN, DV, 256> vreg;
-  const bool general = route == kRouteGeneral;
-  int kid_r = 0, kpos_r = 0;
-  auto load_tile = [&](int kt) {
+  auto stage = [&](int buf) { return smem + buf * C::STAGE_BYTES; };
+  auto issue = [&](int kt, int buf) {
+    T* Ks = reinterpret_cast<T*>(stage(buf));
+    T* Vs = Ks + BN * DQK;
+    int* kid = reinterpret_cast<int*>(Vs + BN * DV);
     const int k0 = kt * BN;
     const int nvalid = min(BN, s.Skv - k0);
-    kreg.load(kp + k0 * a.sk.t, a.sk.t, nvalid, tid);
-    vreg.load(vp + k0 * a.sv.t, a.sv.t, nvalid, tid);
-    if (general && tid < BN) {
-      const int j = k0 + tid;
-      kid_r = j < s.Skv ? a.seg.ids_kv[(size_t)b * s.Skv + j] : 0;
-      kpos_r = j < s.Skv ? a.seg.pos_kv[(size_t)b * s.Skv + j] : 0;
+    if (nvalid == BN) {
+      TileLoad<T, BN, DQK, 256>::direct(kp + k0 * a.sk.t, a.sk.t, Ks, tid);
+      TileLoad<T, BN, DV, 256>::direct(vp + k0 * a.sv.t, a.sv.t, Vs, tid);
+    } else {
+      TileLoad<T, BN, DQK, 256>::staged(kp + k0 * a.sk.t, a.sk.t, nvalid, Ks, tid);
+      TileLoad<T, BN, DV, 256>::staged(vp + k0 * a.sv.t, a.sv.t, nvalid, Vs, tid);
     }
-  };
-  auto stage_ptr = [&](int buf) { return smem + buf * C::STAGE_BYTES; };
-  auto store_tile = [&](int buf) {
-    char* st = stage_ptr(buf);
-    T* Ks = reinterpret_cast<T*>(st);
-    T* VT = Ks + C::K_ELEMS;
-    int* kid = reinterpret_cast<int*>(VT + C::VT_ELEMS);
-    kreg.store(Ks, C::KSTR, tid);
-    vreg.store_t(VT, C::VTSTR, tid);
-    if (general && tid < BN) {
-      kid[tid] = kid_r;
-      kid[BN + tid] = kpos_r;
-    }
+    if (general) stage_kv_meta<BN>(a.seg, b, s.Skv, k0, kid, tid, nvalid == BN);
   };
 
   const float c2 = s.scale_log2;
-  float m = -INFINITY;
-  float l = 0.f;
+  float m = -INFINITY;   // reference max of the raw scores (rescaled lazily)
+  float l = 0.f;         // this lane half's partial sum of exp2((s - m) * c2)
   f32x16 o[DV / 32];
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
@@ -296,37 +211,31 @@ __global__ void __launch_bounds__(256)
   int cls;
   int kt = next_tile(t_lo, cls);
   int buf = 0;
-  if (kt < t_hi) {
-    load_tile(kt);
-    store_tile(0);
-  }
+  if (kt < t_hi) issue(kt, 0);
+  wait_vm();
   __syncthreads();
 
   while (kt < t_hi) {
     int ncls;
     const int nkt = next_tile(kt + 1, ncls);
-    if (nkt < t_hi) load_tile(nkt);
+    if (C::NBUF == 2 && nkt < t_hi) issue(nkt, buf ^ 1);
 
-    const char* st = stage_ptr(buf);
-    const T* Ks = reinterpret_cast<const T*>(st);
-    const T* VT = Ks + C::K_ELEMS;
-    const int* kid = reinterpret_cast<const int*>(VT + C::VT_ELEMS);
+    const T* Ks = reinterpret_cast<const T*>(stage(buf));
+    const T* Vs = Ks + BN * DQK;
+    const int* kid = reinterpret_cast<const int*>(Vs + BN * DV);
     const int k0 = kt * BN;
 
     // S^T = K Q^T for the tile's 64 keys (two 32-key blocks).
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int t = 0; t < DQK / 16; ++t) {
+    for (int t = 0; t < DQK / 16; ++t)
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const F8 ka = lds8<T>(Ks + (blk * 32 + n) * C::KSTR + 16 * t + 8 * hf);
-        sacc[blk] = mma(ka, qf[t], sacc[blk]);
-      }
-    }
+      for (int blk = 0; blk < 2; ++blk)
+        sacc[blk] = mma(frag_row<T, DQK>(Ks, blk * 32 + n, 16 * t + 8 * hf), qf[t], sacc[blk]);
 
     if (cls == kTilePart) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           const int kk = blk * 32 + 8 * grp + 4 * hf;
@@ -336,26 +245,31 @@ __global__ void __launch_bounds__(256)
             pos4 = *reinterpret_cast<const i32x4*>(kid + BN + kk);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = k0 + kk + i;
-            if (!allowed(route, causal, s.Skv, qi, j, qm, TokMeta{ids4[i], pos4[i]}))
+          for (int i = 0; i < 4; ++i)
+            if (!allowed(route, causal, s.Skv, qi, k0 + kk + i, qm, TokMeta{ids4[i], pos4[i]}))
               sacc[blk][4 * grp + i] = -INFINITY;
-          }
         }
-      }
     }
 
-    // Online softmax: running max and sum per query (lane pair n, n + 32).
+    // Online softmax with a lazily updated reference max: the accumulators
+    // are rescaled only when the running max grows by more than 2^8 in
+    // probability terms, so most tiles skip the O rescale entirely.
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[blk][r]);
     mx = wave_xor32_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float mc = m_use * c2;
-    const float alpha = fast_exp2((m - m_use) * c2);
+    const bool grow = mx > m && (m == -INFINITY || (mx - m) * c2 > 8.f);
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m;
+      const float alpha = grow ? fast_exp2((m - m_new) * c2) : 1.f;
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+      m = m_new;
+    }
+    const float mc = (m == -INFINITY ? 0.f : m) * c2;
     float rs = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -365,32 +279,24 @@ __global__ void __launch_bounds__(256)
         sacc[blk][r] = p;
         rs += p;
       }
-    l = l * alpha + rs;
-    m = m_new;
-    if (!__all(alpha == 1.f)) {
-#pragma unroll
-      for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
-    }
+    l += rs;
 
-    // O^T += V^T P^T.
-    F8 pf[2][2];
+    // O^T += V^T P^T, V^T read from the row-major V tile by transpose loads.
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) pf[blk][s2] = E::cvt8(slots8(sacc[blk], s2));
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const F8 pf = E::cvt8(slots8(sacc[blk], s2));
 #pragma unroll
-    for (int d = 0; d < DV / 32; ++d) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const F8 va = lds8<T>(VT + (d * 32 + n) * C::VTSTR + blk * 32 + 16 * s2 + 8 * hf);
-          o[d] = mma(va, pf[blk][s2], o[d]);
-        }
-    }
+        for (int d = 0; d < DV / 32; ++d)
+          o[d] = mma(frag_tr<T, DV>(Vs, d * 32, blk * 32 + 16 * s2, lane), pf, o[d]);
+      }
 
-    if (C::NBUF == 1) __syncthreads();
-    if (nkt < t_hi) store_tile(C::NBUF == 2 ? buf ^ 1 : buf);
+    if (C::NBUF == 1) {
+      __syncthreads();
+      if (nkt < t_hi) issue(nkt, buf);
+    }
+    wait_vm();
     __syncthreads();
     if (C::NBUF == 2) buf ^= 1;
     kt = nkt;
@@ -460,24 +366,21 @@ template <typename T, int DQK, int DV>
 struct DqCfg {
   static constexpr int BM = 128;
   static constexpr int BN = 64;
-  static constexpr int KSTR = DQK + 8;
-  static constexpr int KTSTR = BN + 8;
-  static constexpr int VSTR = DV + 8;
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int KT_ELEMS = DQK * KTSTR;
-  static constexpr int V_ELEMS = BN * VSTR;
-  static constexpr int META_BYTES = 2 * BN * 4;
-  static constexpr int STAGE_BYTES = (K_ELEMS + KT_ELEMS + V_ELEMS) * (int)sizeof(T) + META_BYTES;
-  static constexpr int NBUF = (2 * STAGE_BYTES <= 160 * 1024) ? 2 : 1;
+  static constexpr int K_BYTES = BN * DQK * (int)sizeof(T);
+  static constexpr int V_BYTES = BN * DV * (int)sizeof(T);
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES + 2 * BN * 4;
+  static constexpr int NBUF = Staging<T, STAGE_BYTES>::NBUF;
+  static constexpr int WAVES_PER_EU = Staging<T, STAGE_BYTES>::WAVES_PER_EU;
 };
 
 template <typename T, int DQK, int DV>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, DQK, DV>::WAVES_PER_EU)))
+    attn_bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<T, DQK, DV>;
   using E = Elem<T>;
   using F8 = typename E::F8;
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __attribute__((aligned(16))) char smem[C::NBUF * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE_BYTES];
 
   const AttnShape& s = a.s;
   const bool causal = s.causal != 0;
@@ -520,6 +423,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a) {
   const float delta = qi < s.Sq ? a.delta[rowx] : 0.f;
 
   const int route = s.has_meta ? a.seg.route[b] : kRouteDense;
+  const bool general = route == kRouteGeneral;
   const TokMeta qm = q_meta(route, a.seg, b, s.Sq, qi);
   TileSum qs{};
   const ChunkSum* sum_kv_row = nullptr;
@@ -544,36 +448,21 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a) {
     cls = kTileSkip;
     return t_hi;
   };
-
-  PairTile<T, BN, DQK, 256> kreg;
-  RowTile<T, BN, DV, 256> vreg;
-  const bool general = route == kRouteGeneral;
-  int kid_r = 0, kpos_r = 0;
-  auto load_tile = [&](int kt) {
+  auto stage = [&](int buf) { return smem + buf * C::STAGE_BYTES; };
+  auto issue = [&](int kt, int buf) {
+    T* Ks = reinterpret_cast<T*>(stage(buf));
+    T* Vs = Ks + BN * DQK;
+    int* kid = reinterpret_cast<int*>(Vs + BN * DV);
     const int k0 = kt * BN;
     const int nvalid = min(BN, s.Skv - k0);
-    kreg.load(kp + k0 * a.sk.t, a.sk.t, nvalid, tid);
-    vreg.load(vp + k0 * a.sv.t, a.sv.t, nvalid, tid);
-    if (general && tid < BN) {
-      const int j = k0 + tid;
-      kid_r = j < s.Skv ? a.seg.ids_kv[(size_t)b * s.Skv + j] : 0;
-      kpos_r = j < s.Skv ? a.seg.pos_kv[(size_t)b * s.Skv + j] : 0;
+    if (nvalid == BN) {
+      TileLoad<T, BN, DQK, 256>::direct(kp + k0 * a.sk.t, a.sk.t, Ks, tid);
+      TileLoad<T, BN, DV, 256>::direct(vp + k0 * a.sv.t, a.sv.t, Vs, tid);
+    } else {
+      TileLoad<T, BN, DQK, 256>::staged(kp + k0 * a.sk.t, a.sk.t, nvalid, Ks, tid);
+      TileLoad<T, BN, DV, 256>::staged(vp + k0 * a.sv.t, a.sv.t, nvalid, Vs, tid);
     }
-  };
-  auto stage_ptr = [&](int buf) { return smem + buf * C::STAGE_BYTES; };
-  auto store_tile = [&](int buf) {
-    char* st = stage_ptr(buf);
-    T* Ks = reinterpret_cast<T*>(st);
-    T* KT = Ks + C::K_ELEMS;
-    T* Vs = KT + C::KT_ELEMS;
-    int* kid = reinterpret_cast<int*>(Vs + C::V_ELEMS);
-    kreg.store_rows(Ks, C::KSTR, tid);
-    kreg.store_t(KT, C::KTSTR, tid);
-    vreg.store(Vs, C::VSTR, tid);
-    if (general && tid < BN) {
-      kid[tid] = kid_r;
-      kid[BN + tid] = kpos_r;
-    }
+    if (general) stage_kv_meta<BN>(a.seg, b, s.Skv, k0, kid, tid, nvalid == BN);
   };
 
   const float c2 = s.scale_log2;
@@ -584,40 +473,29 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a) {
   int cls;
   int kt = next_tile(t_lo, cls);
   int buf = 0;
-  if (kt < t_hi) {
-    load_tile(kt);
-    store_tile(0);
-  }
+  if (kt < t_hi) issue(kt, 0);
+  wait_vm();
   __syncthreads();
 
   while (kt < t_hi) {
     int ncls;
     const int nkt = next_tile(kt + 1, ncls);
-    if (nkt < t_hi) load_tile(nkt);
+    if (C::NBUF == 2 && nkt < t_hi) issue(nkt, buf ^ 1);
 
-    const char* st = stage_ptr(buf);
-    const T* Ks = reinterpret_cast<const T*>(st);
-    const T* KT = Ks + C::K_ELEMS;
-    const T* Vs = KT + C::KT_ELEMS;
-    const int* kid = reinterpret_cast<const int*>(Vs + C::V_ELEMS);
+    const T* Ks = reinterpret_cast<const T*>(stage(buf));
+    const T* Vs = Ks + BN * DQK;
+    const int* kid = reinterpret_cast<const int*>(Vs + BN * DV);
     const int k0 = kt * BN;
 
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-    f32x16 pacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int t = 0; t < DQK / 16; ++t)
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        sacc[blk] = mma(lds8<T>(Ks + (blk * 32 + n) * C::KSTR + 16 * t + 8 * hf), qf[t], sacc[blk]);
-#pragma unroll
-    for (int t = 0; t < DV / 16; ++t)
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        pacc[blk] = mma(lds8<T>(Vs + (blk * 32 + n) * C::VSTR + 16 * t + 8 * hf), dof[t], pacc[blk]);
-
-    // P = exp2(S * scale * log2e - LSE2); dS = P * (dP - Delta).
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
+      // S^T and dP^T for 32 keys x this wave's 32 queries.
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DQK / 16; ++t) sacc = mma(frag_row<T, DQK>(Ks, blk * 32 + n, 16 * t + 8 * hf), qf[t], sacc);
+#pragma unroll
+      for (int t = 0; t < DV / 16; ++t) pacc = mma(frag_row<T, DV>(Vs, blk * 32 + n, 16 * t + 8 * hf), dof[t], pacc);
+      // P = exp2(S * scale * log2e - LSE2); dS = P * (dP - Delta).
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int kk = blk * 32 + 8 * grp + 4 * hf;
@@ -629,30 +507,27 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * grp + i;
-          float p = fast_exp2(fmaf(sacc[blk][r], c2, -lse2));
+          float p = fast_exp2(fmaf(sacc[r], c2, -lse2));
           if (cls == kTilePart && !allowed(route, causal, s.Skv, qi, k0 + kk + i, qm, TokMeta{ids4[i], pos4[i]}))
             p = 0.f;
-          sacc[blk][r] = p * (pacc[blk][r] - delta);
+          sacc[r] = p * (pacc[r] - delta);
         }
+      }
+      // dQ^T += K^T dS^T, K^T read from the row-major K tile by transpose loads.
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const F8 dsf = E::cvt8(slots8(sacc, s2));
+#pragma unroll
+        for (int d = 0; d < DQK / 32; ++d)
+          dqa[d] = mma(frag_tr<T, DQK>(Ks, d * 32, blk * 32 + 16 * s2, lane), dsf, dqa[d]);
       }
     }
 
-    // dQ^T += K^T dS^T.
-    F8 dsf[2][2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) dsf[blk][s2] = E::cvt8(slots8(sacc[blk], s2));
-#pragma unroll
-    for (int d = 0; d < DQK / 32; ++d)
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          dqa[d] = mma(lds8<T>(KT + (d * 32 + n) * C::KTSTR + blk * 32 + 16 * s2 + 8 * hf), dsf[blk][s2], dqa[d]);
-
-    if (C::NBUF == 1) __syncthreads();
-    if (nkt < t_hi) store_tile(C::NBUF == 2 ? buf ^ 1 : buf);
+    if (C::NBUF == 1) {
+      __syncthreads();
+      if (nkt < t_hi) issue(nkt, buf);
+    }
+    wait_vm();
     __syncthreads();
     if (C::NBUF == 2) buf ^= 1;
     kt = nkt;
@@ -677,26 +552,25 @@ template <typename T, int DQK, int DV>
 struct DkvCfg {
   static constexpr int BN = 128;   // keys per workgroup (32 per wave)
   static constexpr int BM = 64;    // queries per step
-  static constexpr int QSTR = DQK + 8;
-  static constexpr int QTSTR = BM + 8;
-  static constexpr int DOSTR = DV + 8;
-  static constexpr int DOTSTR = BM + 8;
-  static constexpr int Q_ELEMS = BM * QSTR;
-  static constexpr int QT_ELEMS = DQK * QTSTR;
-  static constexpr int DO_ELEMS = BM * DOSTR;
-  static constexpr int DOT_ELEMS = DV * DOTSTR;
-  static constexpr int SIDE_BYTES = BM * 4 * 4;   // lse2, delta, meta (a, b)
-  static constexpr int STAGE_BYTES = (Q_ELEMS + QT_ELEMS + DO_ELEMS + DOT_ELEMS) * (int)sizeof(T) + SIDE_BYTES;
-  static constexpr int NBUF = (2 * STAGE_BYTES <= 160 * 1024) ? 2 : 1;
+  static constexpr int Q_BYTES = BM * DQK * (int)sizeof(T);
+  static constexpr int DO_BYTES = BM * DV * (int)sizeof(T);
+  static constexpr int SIDE_BYTES = BM * 4 * 4;   // lse2, delta, metadata (a, b)
+  static constexpr int STAGE_BYTES = Q_BYTES + DO_BYTES + SIDE_BYTES;
+  static constexpr int NBUF = Staging<T, STAGE_BYTES>::NBUF;
+  // K, V fragments and the dK, dV accumulators alone take 192 registers per
+  // lane; with the rest this kernel needs more than 256, so one wave per SIMD.
+  static constexpr int WAVES_PER_EU = 1;
 };
 
 template <typename T, int DQK, int DV>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg<T, DQK, DV>::WAVES_PER_EU)))
+    attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = DkvCfg<T, DQK, DV>;
   using E = Elem<T>;
   using F8 = typename E::F8;
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __attribute__((aligned(16))) char smem[C::NBUF * C::STAGE_BYTES];
+  static_assert(BM == 64, "one wave per side row");
+  __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE_BYTES];
 
   const AttnShape& s = a.s;
   const bool causal = s.causal != 0;
@@ -743,60 +617,62 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(BwdArgs a) {
   const int t_lo = lo / BM;
   const int t_hi = (hi + BM - 1) / BM;
   const int ntiles = t_hi - t_lo;
+  const int nsteps = g * ntiles;
 
+  // Steps walk the query tiles from the last one down, and the query heads
+  // of the group inside each tile: workgroups of one key/value head then
+  // read the same query tiles at about the same time (L2 reuse).
+  auto tile_of = [&](int x) { return t_hi - 1 - x / g; };
   auto classify = [&](int qt) -> int {
     TileSum qs{};
     if (route != kRouteDense) qs = tile_sum(sum_q_row, a.seg.nch_q, qt * BM, BM);
     return classify_tile(route, causal, s.Skv, qt * BM, BM, k0, BN, qs, ks);
   };
-  // Steps run over (query head in group, query tile) in a fixed order.
-  auto next_step = [&](int step, int& cls) -> int {
-    for (int x = step; x < g * ntiles; ++x) {
-      cls = classify(t_lo + x % ntiles);
+  auto next_step = [&](int x, int& cls) -> int {
+    while (x < nsteps) {
+      cls = classify(tile_of(x));
       if (cls != kTileSkip) return x;
+      x = (x / g + 1) * g;   // the whole tile is skipped for every head
     }
     cls = kTileSkip;
-    return g * ntiles;
+    return nsteps;
   };
-
-  PairTile<T, BM, DQK, 256> qreg;
-  PairTile<T, BM, DV, 256> doreg;
-  float side_r = 0.f;
-  int meta_r = 0;
-  auto load_step = [&](int x) {
-    const int h = hkv * g + x / ntiles;
-    const int i0 = (t_lo + x % ntiles) * BM;
+  auto stage = [&](int buf) { return smem + buf * C::STAGE_BYTES; };
+  auto issue = [&](int x, int buf) {
+    T* Qs = reinterpret_cast<T*>(stage(buf));
+    T* dOs = Qs + BM * DQK;
+    float* side = reinterpret_cast<float*>(dOs + BM * DV);
+    const int h = hkv * g + x % g;
+    const int i0 = tile_of(x) * BM;
     const int nvalid = min(BM, s.Sq - i0);
-    qreg.load(static_cast<const T*>(a.q) + b * a.sq.b + h * a.sq.h + i0 * a.sq.t, a.sq.t, nvalid, tid);
-    doreg.load(static_cast<const T*>(a.dout) + b * a.so.b + h * a.so.h + i0 * a.so.t, a.so.t, nvalid, tid);
-    // threads 0..63: lse2, 64..127: delta, 128..191: meta a, 192..255: meta b
-    const int r = tid & (BM - 1);
-    const int i = i0 + r;
-    const int which = tid / BM;
-    if (which < 2) {
-      const size_t x2 = ((size_t)b * s.Hq + h) * s.Sq + i;
-      side_r = i < s.Sq ? (which == 0 ? a.lse2[x2] : a.delta[x2]) : (which == 0 ? INFINITY : 0.f);
+    const T* qg = static_cast<const T*>(a.q) + b * a.sq.b + h * a.sq.h + i0 * a.sq.t;
+    const T* dg = static_cast<const T*>(a.dout) + b * a.so.b + h * a.so.h + i0 * a.so.t;
+    const size_t rowx = ((size_t)b * s.Hq + h) * s.Sq + i0;
+    const size_t rowm = (size_t)b * s.Sq + i0;
+    if (nvalid == BM) {
+      TileLoad<T, BM, DQK, 256>::direct(qg, a.sq.t, Qs, tid);
+      TileLoad<T, BM, DV, 256>::direct(dg, a.so.t, dOs, tid);
+      const int* src;
+      if (wave == 0) src = reinterpret_cast<const int*>(a.lse2 + rowx) + lane;
+      else if (wave == 1) src = reinterpret_cast<const int*>(a.delta + rowx) + lane;
+      else if (route == kRouteFast) src = reinterpret_cast<const int*>(a.seg.run_q + rowm + lane) + (wave - 2);
+      else if (route == kRouteGeneral) src = (wave == 2 ? a.seg.ids_q : a.seg.pos_q) + rowm + lane;
+      else src = nullptr;
+      if (src) __builtin_amdgcn_global_load_lds(src, (BPS_LDS void*)(side + wave * BM), 4, 0, 0);
     } else {
-      const TokMeta t = q_meta(route, a.seg, b, s.Sq, i);
-      meta_r = which == 2 ? t.a : t.b;
+      TileLoad<T, BM, DQK, 256>::staged(qg, a.sq.t, nvalid, Qs, tid);
+      TileLoad<T, BM, DV, 256>::staged(dg, a.so.t, nvalid, dOs, tid);
+      const int r = lane;
+      const bool in = r < nvalid;
+      if (wave == 0) {
+        side[r] = in ? a.lse2[rowx + r] : INFINITY;
+      } else if (wave == 1) {
+        side[BM + r] = in ? a.delta[rowx + r] : 0.f;
+      } else {
+        const TokMeta t = in ? q_meta(route, a.seg, b, s.Sq, i0 + r) : TokMeta{0, 0};
+        reinterpret_cast<int*>(side)[wave * BM + r] = wave == 2 ? t.a : t.b;
+      }
     }
-  };
-  auto stage_ptr = [&](int buf) { return smem + buf * C::STAGE_BYTES; };
-  auto store_step = [&](int buf) {
-    char* st = stage_ptr(buf);
-    T* Qs = reinterpret_cast<T*>(st);
-    T* QT = Qs + C::Q_ELEMS;
-    T* dOs = QT + C::QT_ELEMS;
-    T* dOT = dOs + C::DO_ELEMS;
-    float* side = reinterpret_cast<float*>(dOT + C::DOT_ELEMS);
-    qreg.store_rows(Qs, C::QSTR, tid);
-    qreg.store_t(QT, C::QTSTR, tid);
-    doreg.store_rows(dOs, C::DOSTR, tid);
-    doreg.store_t(dOT, C::DOTSTR, tid);
-    if (tid < 2 * BM)
-      side[tid] = side_r;
-    else
-      reinterpret_cast<int*>(side)[tid] = meta_r;
   };
 
   const float c2 = s.scale_log2;
@@ -810,36 +686,31 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(BwdArgs a) {
   int cls;
   int x = next_step(0, cls);
   int buf = 0;
-  if (x < g * ntiles) {
-    load_step(x);
-    store_step(0);
-  }
+  if (x < nsteps) issue(x, 0);
+  wait_vm();
   __syncthreads();
 
-  while (x < g * ntiles) {
+  while (x < nsteps) {
     int ncls;
     const int nx = next_step(x + 1, ncls);
-    if (nx < g * ntiles) load_step(nx);
+    if (C::NBUF == 2 && nx < nsteps) issue(nx, buf ^ 1);
 
-    const char* st = stage_ptr(buf);
-    const T* Qs = reinterpret_cast<const T*>(st);
-    const T* QT = Qs + C::Q_ELEMS;
-    const T* dOs = QT + C::QT_ELEMS;
-    const T* dOT = dOs + C::DO_ELEMS;
-    const float* lse2s = reinterpret_cast<const float*>(dOT + C::DOT_ELEMS);
+    const T* Qs = reinterpret_cast<const T*>(stage(buf));
+    const T* dOs = Qs + BM * DQK;
+    const float* lse2s = reinterpret_cast<const float*>(dOs + BM * DV);
     const float* deltas = lse2s + BM;
     const int* qma = reinterpret_cast<const int*>(lse2s + 2 * BM);
     const int* qmb = qma + BM;
-    const int i0 = (t_lo + x % ntiles) * BM;
+    const int i0 = tile_of(x) * BM;
 
 #pragma unroll
     for (int qb = 0; qb < BM / 32; ++qb) {
       // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
       f32x16 sa = f32x16{}, pa = f32x16{};
 #pragma unroll
-      for (int t = 0; t < DQK / 16; ++t) sa = mma(lds8<T>(Qs + (qb * 32 + n) * C::QSTR + 16 * t + 8 * hf), kf[t], sa);
+      for (int t = 0; t < DQK / 16; ++t) sa = mma(frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf), kf[t], sa);
 #pragma unroll
-      for (int t = 0; t < DV / 16; ++t) pa = mma(lds8<T>(dOs + (qb * 32 + n) * C::DOSTR + 16 * t + 8 * hf), vf[t], pa);
+      for (int t = 0; t < DV / 16; ++t) pa = mma(frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf), vf[t], pa);
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int rr = qb * 32 + 8 * grp + 4 * hf;
@@ -860,27 +731,29 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(BwdArgs a) {
           pa[r] = p * (pa[r] - d4[i]);
         }
       }
-      F8 pf[2], dsf[2];
+      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries (dO^T and
+      // Q^T by transpose loads from the row-major tiles).
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        pf[s2] = E::cvt8(slots8(sa, s2));
-        dsf[s2] = E::cvt8(slots8(pa, s2));
+        const F8 pf = E::cvt8(slots8(sa, s2));
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d)
+          dva[d] = mma(frag_tr<T, DV>(dOs, d * 32, qb * 32 + 16 * s2, lane), pf, dva[d]);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
 #pragma unroll
-      for (int d = 0; d < DV / 32; ++d)
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const F8 dsf = E::cvt8(slots8(pa, s2));
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          dva[d] = mma(lds8<T>(dOT + (d * 32 + n) * C::DOTSTR + qb * 32 + 16 * s2 + 8 * hf), pf[s2], dva[d]);
-#pragma unroll
-      for (int d = 0; d < DQK / 32; ++d)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          dka[d] = mma(lds8<T>(QT + (d * 32 + n) * C::QTSTR + qb * 32 + 16 * s2 + 8 * hf), dsf[s2], dka[d]);
+        for (int d = 0; d < DQK / 32; ++d)
+          dka[d] = mma(frag_tr<T, DQK>(Qs, d * 32, qb * 32 + 16 * s2, lane), dsf, dka[d]);
+      }
     }
 
-    if (C::NBUF == 1) __syncthreads();
-    if (nx < g * ntiles) store_step(C::NBUF == 2 ? buf ^ 1 : buf);
+    if (C::NBUF == 1) {
+      __syncthreads();
+      if (nx < nsteps) issue(nx, buf);
+    }
+    wait_vm();
     __syncthreads();
     if (C::NBUF == 2) buf ^= 1;
     x = nx;
