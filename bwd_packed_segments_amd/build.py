@@ -56,9 +56,10 @@ def units():
     out.append(("seg_meta", [os.path.join(CSRC, "seg_meta.hip")], []))
     out.append(("attn_api", ["-x", "hip", os.path.join(CSRC, "attn_api.cpp")], []))
     for t, dqk, dv in INSTANCES:
-        name = f"attn_{t}_{dqk}_{dv}"
-        out.append((name, [os.path.join(CSRC, "attn_inst.hip")],
-                    [f"-DINST_T={t}", f"-DINST_DQK={dqk}", f"-DINST_DV={dv}"]))
+        for part, tag in ((0, "fwd"), (1, "dq"), (2, "dkdv")):
+            name = f"attn_{tag}_{t}_{dqk}_{dv}"
+            out.append((name, [os.path.join(CSRC, "attn_inst.hip")],
+                        [f"-DINST_T={t}", f"-DINST_DQK={dqk}", f"-DINST_DV={dv}", f"-DINST_PART={part}"]))
     return out
 
 

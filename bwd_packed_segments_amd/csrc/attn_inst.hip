@@ -1,16 +1,21 @@
-// One translation unit per (element type, Dqk, Dv): the build compiles this
-// file once for every head-dim pair the library supports, with INST_T,
-// INST_DQK and INST_DV set on the command line, so the instantiations build
-// in parallel.
+// One translation unit per (element type, Dqk, Dv, kernel family): the build
+// compiles this file once for every combination, with INST_T, INST_DQK,
+// INST_DV and INST_PART (0 forward, 1 Delta + dQ, 2 dK/dV) set on the command
+// line.  Keeping the kernel families apart also keeps the code generated for
+// one from depending on the others.
 #include "attn_kernels.hpp"
 
-#if !defined(INST_T) || !defined(INST_DQK) || !defined(INST_DV)
-#error "INST_T, INST_DQK and INST_DV must be defined"
+#if !defined(INST_T) || !defined(INST_DQK) || !defined(INST_DV) || !defined(INST_PART)
+#error "INST_T, INST_DQK, INST_DV and INST_PART must be defined"
 #endif
 
 namespace bps {
+#if INST_PART == 0
 template hipError_t launch_fwd<INST_T, INST_DQK, INST_DV>(const FwdArgs&, hipStream_t);
+#elif INST_PART == 1
 template hipError_t launch_bwd_delta<INST_T, INST_DQK, INST_DV>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd_dkdv<INST_T, INST_DQK, INST_DV>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<INST_T, INST_DQK, INST_DV>(const BwdArgs&, hipStream_t);
+#else
+template hipError_t launch_bwd_dkdv<INST_T, INST_DQK, INST_DV>(const BwdArgs&, hipStream_t);
+#endif
 }  // namespace bps

@@ -236,19 +236,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
     if (cls == kTilePart) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int kk = blk * 32 + 8 * grp + 4 * hf;
-          i32x4 ids4 = i32x4{0, 0, 0, 0}, pos4 = i32x4{0, 0, 0, 0};
-          if (general) {
-            ids4 = *reinterpret_cast<const i32x4*>(kid + kk);
-            pos4 = *reinterpret_cast<const i32x4*>(kid + BN + kk);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!allowed(route, causal, s.Skv, qi, k0 + kk + i, qm, TokMeta{ids4[i], pos4[i]}))
-              sacc[blk][4 * grp + i] = -INFINITY;
-        }
+        mask_tile<true>(sacc[blk], -INFINITY, route, causal, s.Skv, qi, qm, k0 + blk * 32, hf, kid, kid + BN, blk * 32);
     }
 
     // Online softmax with a lazily updated reference max: the accumulators
@@ -370,7 +358,9 @@ struct DqCfg {
   static constexpr int V_BYTES = BN * DV * (int)sizeof(T);
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES + 2 * BN * 4;
   static constexpr int NBUF = Staging<T, STAGE_BYTES>::NBUF;
-  static constexpr int WAVES_PER_EU = Staging<T, STAGE_BYTES>::WAVES_PER_EU;
+  // Q, dO fragments and the dQ accumulator outgrow half the register file
+  // for wide heads.
+  static constexpr int WAVES_PER_EU = (DQK > 128 || DQK + DV > 256) ? 1 : Staging<T, STAGE_BYTES>::WAVES_PER_EU;
 };
 
 template <typename T, int DQK, int DV>
@@ -497,22 +487,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<
       for (int t = 0; t < DV / 16; ++t) pacc = mma(frag_row<T, DV>(Vs, blk * 32 + n, 16 * t + 8 * hf), dof[t], pacc);
       // P = exp2(S * scale * log2e - LSE2); dS = P * (dP - Delta).
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int kk = blk * 32 + 8 * grp + 4 * hf;
-        i32x4 ids4 = i32x4{0, 0, 0, 0}, pos4 = i32x4{0, 0, 0, 0};
-        if (cls == kTilePart && general) {
-          ids4 = *reinterpret_cast<const i32x4*>(kid + kk);
-          pos4 = *reinterpret_cast<const i32x4*>(kid + BN + kk);
-        }
+      for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c2, -lse2));
+      if (cls == kTilePart)
+        mask_tile<true>(sacc, 0.f, route, causal, s.Skv, qi, qm, k0 + blk * 32, hf, kid, kid + BN, blk * 32);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * grp + i;
-          float p = fast_exp2(fmaf(sacc[r], c2, -lse2));
-          if (cls == kTilePart && !allowed(route, causal, s.Skv, qi, k0 + kk + i, qm, TokMeta{ids4[i], pos4[i]}))
-            p = 0.f;
-          sacc[r] = p * (pacc[r] - delta);
-        }
-      }
+      for (int r = 0; r < 16; ++r) sacc[r] = sacc[r] * (pacc[r] - delta);
       // dQ^T += K^T dS^T, K^T read from the row-major K tile by transpose loads.
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -551,12 +530,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<
 template <typename T, int DQK, int DV>
 struct DkvCfg {
   static constexpr int BN = 128;   // keys per workgroup (32 per wave)
-  static constexpr int BM = 64;    // queries per step
+  // Queries per step: two 32-row blocks, one for wide heads and fp32 (the
+  // transposed operands of a step are held in registers).
+  static constexpr int BM = (sizeof(T) == 4 || DQK > 128 || DQK + DV > 256) ? 32 : 64;
   static constexpr int Q_BYTES = BM * DQK * (int)sizeof(T);
   static constexpr int DO_BYTES = BM * DV * (int)sizeof(T);
   static constexpr int SIDE_BYTES = BM * 4 * 4;   // lse2, delta, metadata (a, b)
   static constexpr int STAGE_BYTES = Q_BYTES + DO_BYTES + SIDE_BYTES;
-  static constexpr int NBUF = Staging<T, STAGE_BYTES>::NBUF;
+  // Three buffers: the loads for step x + 2 are issued when step x ends, so
+  // they have a whole step to land (one workgroup per CU, see below).
+  static constexpr int NBUF = (3 * STAGE_BYTES <= 160 * 1024) ? 3 : 1;
   // K, V fragments and the dK, dV accumulators alone take 192 registers per
   // lane; with the rest this kernel needs more than 256, so one wave per SIMD.
   static constexpr int WAVES_PER_EU = 1;
@@ -569,7 +552,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
   using E = Elem<T>;
   using F8 = typename E::F8;
   constexpr int BM = C::BM, BN = C::BN;
-  static_assert(BM == 64, "one wave per side row");
+  static_assert(BM == 32 || BM == 64, "one wave per side row");
   __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE_BYTES];
 
   const AttnShape& s = a.s;
@@ -637,9 +620,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
     cls = kTileSkip;
     return nsteps;
   };
-  auto stage = [&](int buf) { return smem + buf * C::STAGE_BYTES; };
-  auto issue = [&](int x, int buf) {
-    T* Qs = reinterpret_cast<T*>(stage(buf));
+
+  // Q, dO and the per-row side data of a step go straight from global memory
+  // to LDS (through registers with zero fill for the last, partial tile).
+  // Returns whether the loads are still in flight.
+  auto issue = [&](int x, char* st) -> bool {
+    T* Qs = reinterpret_cast<T*>(st);
     T* dOs = Qs + BM * DQK;
     float* side = reinterpret_cast<float*>(dOs + BM * DV);
     const int h = hkv * g + x % g;
@@ -652,18 +638,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
     if (nvalid == BM) {
       TileLoad<T, BM, DQK, 256>::direct(qg, a.sq.t, Qs, tid);
       TileLoad<T, BM, DV, 256>::direct(dg, a.so.t, dOs, tid);
+      // wave 0: LSE in base 2, wave 1: Delta, waves 2 and 3: row metadata
       const int* src;
       if (wave == 0) src = reinterpret_cast<const int*>(a.lse2 + rowx) + lane;
       else if (wave == 1) src = reinterpret_cast<const int*>(a.delta + rowx) + lane;
       else if (route == kRouteFast) src = reinterpret_cast<const int*>(a.seg.run_q + rowm + lane) + (wave - 2);
       else if (route == kRouteGeneral) src = (wave == 2 ? a.seg.ids_q : a.seg.pos_q) + rowm + lane;
       else src = nullptr;
-      if (src) __builtin_amdgcn_global_load_lds(src, (BPS_LDS void*)(side + wave * BM), 4, 0, 0);
-    } else {
-      TileLoad<T, BM, DQK, 256>::staged(qg, a.sq.t, nvalid, Qs, tid);
-      TileLoad<T, BM, DV, 256>::staged(dg, a.so.t, nvalid, dOs, tid);
-      const int r = lane;
-      const bool in = r < nvalid;
+      if (src && lane < BM) __builtin_amdgcn_global_load_lds(src, (BPS_LDS void*)(side + wave * BM), 4, 0, 0);
+      return true;
+    }
+    TileLoad<T, BM, DQK, 256>::staged(qg, a.sq.t, nvalid, Qs, tid);
+    TileLoad<T, BM, DV, 256>::staged(dg, a.so.t, nvalid, dOs, tid);
+    const int r = lane;
+    const bool in = r < nvalid;
+    if (r < BM) {
       if (wave == 0) {
         side[r] = in ? a.lse2[rowx + r] : INFINITY;
       } else if (wave == 1) {
@@ -673,6 +662,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
         reinterpret_cast<int*>(side)[wave * BM + r] = wave == 2 ? t.a : t.b;
       }
     }
+    return false;
   };
 
   const float c2 = s.scale_log2;
@@ -683,84 +673,437 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) dva[d] = f32x16{};
 
-  int cls;
-  int x = next_step(0, cls);
-  int buf = 0;
-  if (x < nsteps) issue(x, 0);
-  wait_vm();
-  __syncthreads();
-
-  while (x < nsteps) {
-    int ncls;
-    const int nx = next_step(x + 1, ncls);
-    if (C::NBUF == 2 && nx < nsteps) issue(nx, buf ^ 1);
-
-    const T* Qs = reinterpret_cast<const T*>(stage(buf));
+  // One step over BM queries of one head.  The two 32-query blocks are
+  // interleaved: block 1's S and dP products are issued before block 0's
+  // softmax gradient, and block 0's dV and dK products before block 1's, so
+  // the matrix cores have independent work while the VALU runs (one wave per
+  // SIMD: nothing else would fill those cycles).  part: the tile needs the
+  // element mask.
+  auto compute = [&](const char* st, int x, bool part) {
+    const T* Qs = reinterpret_cast<const T*>(st);
     const T* dOs = Qs + BM * DQK;
     const float* lse2s = reinterpret_cast<const float*>(dOs + BM * DV);
     const float* deltas = lse2s + BM;
     const int* qma = reinterpret_cast<const int*>(lse2s + 2 * BM);
     const int* qmb = qma + BM;
     const int i0 = tile_of(x) * BM;
+    constexpr int NQB = BM / 32;
 
+    auto sdp = [&](int qb, f32x16& sa, f32x16& pa) {
+      F8 qa[DQK / 16], da[DV / 16];
 #pragma unroll
-    for (int qb = 0; qb < BM / 32; ++qb) {
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
-      f32x16 sa = f32x16{}, pa = f32x16{};
+      for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
 #pragma unroll
-      for (int t = 0; t < DQK / 16; ++t) sa = mma(frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf), kf[t], sa);
+      for (int t = 0; t < DV / 16; ++t) da[t] = frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf);
+      sa = f32x16{};
+      pa = f32x16{};
 #pragma unroll
-      for (int t = 0; t < DV / 16; ++t) pa = mma(frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf), vf[t], pa);
+      for (int t = 0; t < DQK / 16; ++t) sa = mma(qa[t], kf[t], sa);
+#pragma unroll
+      for (int t = 0; t < DV / 16; ++t) pa = mma(da[t], vf[t], pa);
+    };
+    // P = exp2(S * scale * log2e - LSE2), dS = P * (dP - Delta); returns the
+    // bf16 operands of the dV and dK products.
+    auto softgrad = [&](int qb, f32x16& sa, f32x16& pa, F8* pf, F8* dsf) {
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        const int rr = qb * 32 + 8 * grp + 4 * hf;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + rr);
-        i32x4 ma = i32x4{0, 0, 0, 0}, mb = i32x4{0, 0, 0, 0};
-        if (cls == kTilePart && route != kRouteDense) {
-          ma = *reinterpret_cast<const i32x4*>(qma + rr);
-          mb = *reinterpret_cast<const i32x4*>(qmb + rr);
-        }
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * grp + i;
-          float p = fast_exp2(fmaf(sa[r], c2, -l4[i]));
-          if (cls == kTilePart && !allowed(route, causal, s.Skv, i0 + rr + i, kj, TokMeta{ma[i], mb[i]}, km))
-            p = 0.f;
-          sa[r] = p;
-          pa[r] = p * (pa[r] - d4[i]);
-        }
+        for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[i]));
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries (dO^T and
-      // Q^T by transpose loads from the row-major tiles).
+      if (part) mask_tile<false>(sa, 0.f, route, causal, s.Skv, kj, km, i0 + qb * 32, hf, qma, qmb, qb * 32);
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pa[4 * grp + i] = sa[4 * grp + i] * (pa[4 * grp + i] - d4[i]);
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const F8 pf = E::cvt8(slots8(sa, s2));
+        pf[s2] = E::cvt8(slots8(sa, s2));
+        dsf[s2] = E::cvt8(slots8(pa, s2));
+      }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transpose reads).
+    auto dvdk = [&](int qb, const F8* pf, const F8* dsf) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int d = 0; d < DV / 32; ++d)
-          dva[d] = mma(frag_tr<T, DV>(dOs, d * 32, qb * 32 + 16 * s2, lane), pf, dva[d]);
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const F8 dsf = E::cvt8(slots8(pa, s2));
+          dva[d] = mma(frag_tr<T, DV>(dOs, d * 32, qb * 32 + 16 * s2, lane), pf[s2], dva[d]);
 #pragma unroll
         for (int d = 0; d < DQK / 32; ++d)
-          dka[d] = mma(frag_tr<T, DQK>(Qs, d * 32, qb * 32 + 16 * s2, lane), dsf, dka[d]);
+          dka[d] = mma(frag_tr<T, DQK>(Qs, d * 32, qb * 32 + 16 * s2, lane), dsf[s2], dka[d]);
       }
-    }
+    };
 
-    if (C::NBUF == 1) {
-      __syncthreads();
-      if (nx < nsteps) issue(nx, buf);
+    f32x16 s0, p0;
+    F8 pf0[2], dsf0[2];
+    sdp(0, s0, p0);
+    if constexpr (NQB == 2) {
+      f32x16 s1, p1;
+      F8 pf1[2], dsf1[2];
+      sdp(1, s1, p1);
+      softgrad(0, s0, p0, pf0, dsf0);
+      dvdk(0, pf0, dsf0);
+      softgrad(1, s1, p1, pf1, dsf1);
+      dvdk(1, pf1, dsf1);
+    } else {
+      softgrad(0, s0, p0, pf0, dsf0);
+      dvdk(0, pf0, dsf0);
     }
+  };
+
+  // Loads in flight per thread after a direct issue (the side row load is
+  // left out: waiting for one op fewer than issued still covers it, since
+  // it is the youngest).
+  constexpr int kBatch = TileLoad<T, BM, DQK, 256>::PER + TileLoad<T, BM, DV, 256>::PER;
+  int cls;
+  int x = next_step(0, cls);
+  if constexpr (C::NBUF == 3) {
+    int ncls;
+    const int nx = next_step(x + 1, ncls);
+    if (x < nsteps) issue(x, smem);
+    if (nx < nsteps) issue(nx, smem + C::STAGE_BYTES);
     wait_vm();
     __syncthreads();
-    if (C::NBUF == 2) buf ^= 1;
-    x = nx;
-    cls = ncls;
+    int bi = 0;        // buffer of step x
+    int nnx = nx, nncls = ncls;
+    while (x < nsteps) {
+      char* cur = smem + bi * C::STAGE_BYTES;
+      compute(cur, x, cls == kTilePart);
+      // Step after next into the buffer read in the previous step.
+      int n2cls;
+      const int n2 = nnx < nsteps ? next_step(nnx + 1, n2cls) : nsteps;
+      bool inflight = false;
+      if (n2 < nsteps) inflight = issue(n2, smem + (bi == 0 ? 2 : bi - 1) * C::STAGE_BYTES);
+      if (inflight) wait_vm_keep<kBatch>();
+      else wait_vm();
+      __syncthreads();
+      bi = bi == 2 ? 0 : bi + 1;
+      x = nnx;
+      cls = nncls;
+      nnx = n2;
+      nncls = n2cls;
+    }
+  } else {
+    if (x < nsteps) issue(x, smem);
+    wait_vm();
+    __syncthreads();
+    while (x < nsteps) {
+      int ncls;
+      const int nx = next_step(x + 1, ncls);
+      compute(smem, x, cls == kTilePart);
+      __syncthreads();
+      if (nx < nsteps) issue(nx, smem);
+      wait_vm();
+      __syncthreads();
+      x = nx;
+      cls = ncls;
+    }
   }
 
   if (kj < s.Skv) {
+    T* dkp = static_cast<T*>(a.dk) + b * a.sk.b + kj * a.sk.t + hkv * a.sk.h;
+    T* dvp = static_cast<T*>(a.dv) + b * a.sv.b + kj * a.sv.t + hkv * a.sv.h;
+#pragma unroll
+    for (int d = 0; d < DQK / 32; ++d)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        f32x4 v = f32x4{dka[d][4 * grp], dka[d][4 * grp + 1], dka[d][4 * grp + 2], dka[d][4 * grp + 3]} * s.scale;
+        *reinterpret_cast<typename E::P4*>(dkp + d * 32 + 8 * grp + 4 * hf) = E::cvt4(v);
+      }
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        f32x4 v = f32x4{dva[d][4 * grp], dva[d][4 * grp + 1], dva[d][4 * grp + 2], dva[d][4 * grp + 3]};
+        *reinterpret_cast<typename E::P4*>(dvp + d * 32 + 8 * grp + 4 * hf) = E::cvt4(v);
+      }
+  }
+}
+
+// ------------------------------------------------------------ backward: dK, dV, warp-specialized
+
+// bf16 with head dims up to 128: eight waves, two per SIMD.  Waves 0-3
+// (producers) each own 32 keys: they hold the K and V fragments, compute S
+// and dP for 32 queries, turn them into P and dS (bf16) and pass those
+// through LDS.  Waves 4-7 (consumers) own the same 32 keys: they hold the dK
+// and dV accumulators and run the dV += dO^T P and dK += Q^T dS products one
+// 32-query phase behind.  Producer and consumer of a key block share a SIMD,
+// so the producers' softmax-gradient VALU work overlaps the consumers'
+// matrix work, and each role fits half the register file.  The query tiles
+// are walked and classified exactly as in the kernel above, and every dK/dV
+// element is still written once, at the end, by its consumer wave.
+template <typename T, int DQK, int DV>
+struct DkvWsCfg {
+  static constexpr int BN = 128;   // keys per workgroup: 4 key blocks of 32
+  static constexpr int BM = 64;    // queries per step: 2 phases of 32
+  static constexpr int THREADS = 512;
+  static constexpr int Q_BYTES = BM * DQK * (int)sizeof(T);
+  static constexpr int DO_BYTES = BM * DV * (int)sizeof(T);
+  static constexpr int SIDE_BYTES = BM * 4 * 4;
+  static constexpr int STAGE_BYTES = Q_BYTES + DO_BYTES + SIDE_BYTES;
+  static constexpr int XSLOT_BYTES = 4 * 4 * 64 * 16;   // 4 key blocks x (P, P, dS, dS) x 64 lanes x 16 B
+  static constexpr int LDS_BYTES = 3 * STAGE_BYTES + 2 * XSLOT_BYTES;
+  static constexpr bool ENABLED = sizeof(T) == 2 && DQK <= 128 && DV <= 128 && LDS_BYTES <= 160 * 1024;
+};
+
+template <typename T, int DQK, int DV>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+    attn_bwd_dkdv_ws_kernel(BwdArgs a) {
+  using C = DkvWsCfg<T, DQK, DV>;
+  using E = Elem<T>;
+  using F8 = typename E::F8;
+  constexpr int BM = C::BM, BN = C::BN;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  char* xch = smem + 3 * C::STAGE_BYTES;
+
+  const AttnShape& s = a.s;
+  const bool causal = s.causal != 0;
+  const int n_kt = (s.Skv + BN - 1) / BN;
+  const int g = s.Hq / s.Hkv;
+  const int nblocks = s.B * s.Hkv * n_kt;
+  int L = logical_block(nblocks, s.reverse);
+  const int krank = L % n_kt;
+  L /= n_kt;
+  const int hkv = L % s.Hkv;
+  const int b = L / s.Hkv;
+  const int k0 = krank * BN;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const bool producer = wave < 4;
+  const int kb = wave & 3;                 // key block of this wave
+  const int ptid = tid & 255;              // thread index among producers (loads)
+  const int kj = k0 + kb * 32 + n;
+
+  const int route = s.has_meta ? a.seg.route[b] : kRouteDense;
+  const bool general = route == kRouteGeneral;
+  TileSum ks{};
+  const ChunkSum* sum_q_row = nullptr;
+  if (route != kRouteDense) {
+    ks = tile_sum(a.seg.sum_kv + (size_t)b * a.seg.nch_kv, a.seg.nch_kv, k0, BN);
+    sum_q_row = a.seg.sum_q + (size_t)b * a.seg.nch_q;
+  }
+  int lo, hi;
+  q_range(route, causal, s.Sq, k0, BN, ks, lo, hi);
+  const int t_hi = (hi + BM - 1) / BM;
+  const int ntiles = t_hi - lo / BM;
+  const int nsteps = g * ntiles;
+  auto tile_of = [&](int x) { return t_hi - 1 - x / g; };
+  auto classify = [&](int qt) -> int {
+    TileSum qs{};
+    if (route != kRouteDense) qs = tile_sum(sum_q_row, a.seg.nch_q, qt * BM, BM);
+    return classify_tile(route, causal, s.Skv, qt * BM, BM, k0, BN, qs, ks);
+  };
+  auto next_step = [&](int x, int& cls) -> int {
+    while (x < nsteps) {
+      cls = classify(tile_of(x));
+      if (cls != kTileSkip) return x;
+      x = (x / g + 1) * g;
+    }
+    cls = kTileSkip;
+    return nsteps;
+  };
+
+  // Producer loads of one step (Q, dO, side rows) into a stage buffer;
+  // returns whether they are still in flight.
+  auto issue = [&](int x, char* st) -> bool {
+    T* Qs = reinterpret_cast<T*>(st);
+    T* dOs = Qs + BM * DQK;
+    float* side = reinterpret_cast<float*>(dOs + BM * DV);
+    const int h = hkv * g + x % g;
+    const int i0 = tile_of(x) * BM;
+    const int nvalid = min(BM, s.Sq - i0);
+    const T* qg = static_cast<const T*>(a.q) + b * a.sq.b + h * a.sq.h + i0 * a.sq.t;
+    const T* dg = static_cast<const T*>(a.dout) + b * a.so.b + h * a.so.h + i0 * a.so.t;
+    const size_t rowx = ((size_t)b * s.Hq + h) * s.Sq + i0;
+    const size_t rowm = (size_t)b * s.Sq + i0;
+    if (nvalid == BM) {
+      TileLoad<T, BM, DQK, 256>::direct(qg, a.sq.t, Qs, ptid);
+      TileLoad<T, BM, DV, 256>::direct(dg, a.so.t, dOs, ptid);
+      const int* src;
+      if (wave == 0) src = reinterpret_cast<const int*>(a.lse2 + rowx) + lane;
+      else if (wave == 1) src = reinterpret_cast<const int*>(a.delta + rowx) + lane;
+      else if (route == kRouteFast) src = reinterpret_cast<const int*>(a.seg.run_q + rowm + lane) + (wave - 2);
+      else if (route == kRouteGeneral) src = (wave == 2 ? a.seg.ids_q : a.seg.pos_q) + rowm + lane;
+      else src = nullptr;
+      if (src) __builtin_amdgcn_global_load_lds(src, (BPS_LDS void*)(side + wave * BM), 4, 0, 0);
+      return true;
+    }
+    TileLoad<T, BM, DQK, 256>::staged(qg, a.sq.t, nvalid, Qs, ptid);
+    TileLoad<T, BM, DV, 256>::staged(dg, a.so.t, nvalid, dOs, ptid);
+    const bool in = lane < nvalid;
+    if (wave == 0) {
+      side[lane] = in ? a.lse2[rowx + lane] : INFINITY;
+    } else if (wave == 1) {
+      side[BM + lane] = in ? a.delta[rowx + lane] : 0.f;
+    } else {
+      const TokMeta t = in ? q_meta(route, a.seg, b, s.Sq, i0 + lane) : TokMeta{0, 0};
+      reinterpret_cast<int*>(side)[wave * BM + lane] = wave == 2 ? t.a : t.b;
+    }
+    return false;
+  };
+  auto xfrag = [&](int slot, int f) {
+    return reinterpret_cast<F8*>(xch + slot * C::XSLOT_BYTES) + ((kb * 4 + f) * 64 + lane);
+  };
+
+  const float c2 = s.scale_log2;
+  F8 kf[DQK / 16];
+  F8 vf[DV / 16];
+  TokMeta km{0, 0};
+  f32x16 dka[DQK / 32];
+  f32x16 dva[DV / 32];
+#pragma unroll
+  for (int d = 0; d < DQK / 32; ++d) dka[d] = f32x16{};
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d) dva[d] = f32x16{};
+  if (producer) {
+    const T* kp = static_cast<const T*>(a.k) + b * a.sk.b + hkv * a.sk.h;
+    const T* vp = static_cast<const T*>(a.v) + b * a.sv.b + hkv * a.sv.h;
+#pragma unroll
+    for (int t = 0; t < DQK / 16; ++t)
+      kf[t] = kj < s.Skv ? E::load8(kp + kj * a.sk.t + 16 * t + 8 * hf) : E::zero8();
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t)
+      vf[t] = kj < s.Skv ? E::load8(vp + kj * a.sv.t + 16 * t + 8 * hf) : E::zero8();
+    if (general) km = kv_meta(route, a.seg, b, s.Skv, kj);
+  }
+
+  // Producer phase: S, dP for queries qb*32.. of step x, then P and dS (bf16)
+  // into exchange slot `slot`.
+  auto produce = [&](const char* st, int x, int qb, bool part, int slot) {
+    const T* Qs = reinterpret_cast<const T*>(st);
+    const T* dOs = Qs + BM * DQK;
+    const float* lse2s = reinterpret_cast<const float*>(dOs + BM * DV);
+    const float* deltas = lse2s + BM;
+    const int* qma = reinterpret_cast<const int*>(lse2s + 2 * BM);
+    const int* qmb = qma + BM;
+    F8 qa[DQK / 16], da[DV / 16];
+#pragma unroll
+    for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t) da[t] = frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf);
+    f32x16 sa = f32x16{}, pa = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DQK / 16; ++t) sa = mma(qa[t], kf[t], sa);
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t) pa = mma(da[t], vf[t], pa);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[i]));
+    }
+    if (part) mask_tile<false>(sa, 0.f, route, causal, s.Skv, kj, km, tile_of(x) * BM + qb * 32, hf, qma, qmb, qb * 32);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pa[4 * grp + i] = sa[4 * grp + i] * (pa[4 * grp + i] - d4[i]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      *xfrag(slot, s2) = E::cvt8(slots8(sa, s2));
+      *xfrag(slot, 2 + s2) = E::cvt8(slots8(pa, s2));
+    }
+  };
+  // Consumer phase: dV^T += dO^T P, dK^T += Q^T dS for queries qb*32.. of
+  // the stage (dO^T and Q^T by transpose reads).
+  auto consume = [&](const char* st, int qb, int slot) {
+    const T* Qs = reinterpret_cast<const T*>(st);
+    const T* dOs = Qs + BM * DQK;
+    F8 pf[2], dsf[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      pf[s2] = *xfrag(slot, s2);
+      dsf[s2] = *xfrag(slot, 2 + s2);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+        dva[d] = mma(frag_tr<T, DV>(dOs, d * 32, qb * 32 + 16 * s2, lane), pf[s2], dva[d]);
+#pragma unroll
+      for (int d = 0; d < DQK / 32; ++d)
+        dka[d] = mma(frag_tr<T, DQK>(Qs, d * 32, qb * 32 + 16 * s2, lane), dsf[s2], dka[d]);
+    }
+  };
+
+  // Phase schedule, computed identically by both roles.  Step k (in walk
+  // order, skipped tiles left out) lives in stage buffer k % 3 and takes two
+  // phases (32 queries each).  In phase j the producers handle phase j and
+  // the consumers phase j - 1; every wave passes one barrier per phase.  In
+  // the second phase of step k the producers issue the loads of step k + 2
+  // (into the buffer of step k - 1, which the consumers finished a phase
+  // earlier) and wait for those of step k + 1.
+  struct Sched {
+    int x, cls, nx, ncls, buf, qb;
+  };
+  auto sched_init = [&]() {
+    Sched t;
+    t.x = next_step(0, t.cls);
+    t.nx = t.x < nsteps ? next_step(t.x + 1, t.ncls) : nsteps;
+    t.buf = 0;
+    t.qb = 0;
+    return t;
+  };
+  auto sched_next = [&](Sched& t) {
+    if (t.qb == 0) {
+      t.qb = 1;
+      return;
+    }
+    t.qb = 0;
+    t.x = t.nx;
+    t.cls = t.ncls;
+    t.buf = t.buf == 2 ? 0 : t.buf + 1;
+    t.nx = t.x < nsteps ? next_step(t.x + 1, t.ncls) : nsteps;
+  };
+  constexpr int kBatch = TileLoad<T, BM, DQK, 256>::PER + TileLoad<T, BM, DV, 256>::PER;
+
+  if (producer) {
+    Sched t = sched_init();
+    if (t.x < nsteps) issue(t.x, smem);
+    if (t.nx < nsteps) issue(t.nx, smem + C::STAGE_BYTES);
+    wait_vm();
+    __syncthreads();
+    int slot = 0;
+    while (t.x < nsteps) {
+      bool inflight = false;
+      if (t.qb == 1 && t.nx < nsteps) {
+        int n2cls;
+        const int n2 = next_step(t.nx + 1, n2cls);
+        if (n2 < nsteps) inflight = issue(n2, smem + (t.buf == 0 ? 2 : t.buf - 1) * C::STAGE_BYTES);
+      }
+      produce(smem + t.buf * C::STAGE_BYTES, t.x, t.qb, t.cls == kTilePart, slot);
+      if (t.qb == 1) {       // step k + 1 must be in LDS before its first phase
+        if (inflight) wait_vm_keep<kBatch>();
+        else wait_vm();
+      }
+      __syncthreads();
+      slot ^= 1;
+      sched_next(t);
+    }
+    wait_vm();
+    __syncthreads();   // the consumers' last phase
+  } else {
+    Sched t = sched_init();
+    __syncthreads();   // prologue loads
+    __syncthreads();   // phase 0: the producers' first phase
+    int slot = 0;
+    while (t.x < nsteps) {
+      consume(smem + t.buf * C::STAGE_BYTES, t.qb, slot);
+      __syncthreads();
+      slot ^= 1;
+      sched_next(t);
+    }
+  }
+
+  if (!producer && kj < s.Skv) {
     T* dkp = static_cast<T*>(a.dk) + b * a.sk.b + kj * a.sk.t + hkv * a.sk.h;
     T* dvp = static_cast<T*>(a.dv) + b * a.sv.b + kj * a.sv.t + hkv * a.sv.h;
 #pragma unroll
@@ -806,7 +1149,12 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
   const int n_kt = (a.s.Skv + DkvCfg<T, DQK, DV>::BN - 1) / DkvCfg<T, DQK, DV>::BN;
   const long long nblocks = (long long)a.s.B * a.s.Hkv * n_kt;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  if constexpr (DkvWsCfg<T, DQK, DV>::ENABLED) {
+    static_assert(DkvWsCfg<T, DQK, DV>::BN == DkvCfg<T, DQK, DV>::BN, "same key tiling");
+    hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(512), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -200,10 +200,84 @@ struct TokMeta {
 
 // The element mask.  i, j are token indices inside the batch row; rows past
 // Sq and keys past Skv carry empty metadata (fast: (0,0); general: id 0).
+// One branch-free predicate per route; the kernels pick the route and the
+// causal flag once per tile and apply the predicate with selects.
+template <bool CAUSAL>
+__device__ inline bool allowed_dense(int Skv, int i, int j) {
+  return (j < Skv) & (!CAUSAL | (j <= i));
+}
+template <bool CAUSAL>
+__device__ inline bool allowed_fast(int i, int j, TokMeta qi) {   // qi = run [start, end) of query i
+  return (j >= qi.a) & (j < qi.b) & (!CAUSAL | (j <= i));
+}
+template <bool CAUSAL>
+__device__ inline bool allowed_general(TokMeta qi, TokMeta kj) {  // (segment id, position)
+  return (qi.a != 0) & (qi.a == kj.a) & (!CAUSAL | (kj.b <= qi.b));
+}
+
 __device__ inline bool allowed(int route, bool causal, int Skv, int i, int j, TokMeta qi, TokMeta kj) {
-  if (route == kRouteDense) return j < Skv && (!causal || j <= i);
-  if (route == kRouteFast) return j >= qi.a && j < qi.b && (!causal || j <= i);
-  return qi.a != 0 && qi.a == kj.a && (!causal || kj.b <= qi.b);
+  if (route == kRouteDense) return causal ? allowed_dense<true>(Skv, i, j) : allowed_dense<false>(Skv, i, j);
+  if (route == kRouteFast) return causal ? allowed_fast<true>(i, j, qi) : allowed_fast<false>(i, j, qi);
+  return causal ? allowed_general<true>(qi, kj) : allowed_general<false>(qi, kj);
+}
+
+// Masks one 32x32 accumulator tile held in the C layout: slot r of lane
+// (n, hf) is row rmap(hf, r).  KEYS_IN_ROWS: rows are keys kbase + rmap and
+// the lane's query is fixed (S^T in the forward and dQ kernels); otherwise
+// rows are queries ibase + rmap and the lane's key is fixed (S in the dK/dV
+// kernel).  Per-row metadata of the varying side comes from LDS
+// (meta_a/meta_b, indexed like the rows, offset by moff); masked slots get
+// `fill`.
+template <bool KEYS_IN_ROWS, bool CAUSAL>
+__device__ inline void mask_tile_route(f32x16& x, float fill, int route, int Skv, int fixed_tok, TokMeta fixed,
+                                       int base, int hf, const int* meta_a, const int* meta_b, int moff) {
+  if (route == kRouteDense) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int v = base + rmap(hf, r);
+      const bool ok = KEYS_IN_ROWS ? allowed_dense<CAUSAL>(Skv, fixed_tok, v) : allowed_dense<CAUSAL>(Skv, v, fixed_tok);
+      x[r] = ok ? x[r] : fill;
+    }
+  } else if (route == kRouteFast) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      i32x4 ma = i32x4{0, 0, 0, 0}, mb = i32x4{0, 0, 0, 0};
+      if (!KEYS_IN_ROWS) {
+        ma = *reinterpret_cast<const i32x4*>(meta_a + moff + 8 * grp + 4 * hf);
+        mb = *reinterpret_cast<const i32x4*>(meta_b + moff + 8 * grp + 4 * hf);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        const int v = base + rmap(hf, r);
+        const bool ok = KEYS_IN_ROWS ? allowed_fast<CAUSAL>(fixed_tok, v, fixed)
+                                     : allowed_fast<CAUSAL>(v, fixed_tok, TokMeta{ma[i], mb[i]});
+        x[r] = ok ? x[r] : fill;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const i32x4 ma = *reinterpret_cast<const i32x4*>(meta_a + moff + 8 * grp + 4 * hf);
+      const i32x4 mb = *reinterpret_cast<const i32x4*>(meta_b + moff + 8 * grp + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        const bool ok = KEYS_IN_ROWS ? allowed_general<CAUSAL>(fixed, TokMeta{ma[i], mb[i]})
+                                     : allowed_general<CAUSAL>(TokMeta{ma[i], mb[i]}, fixed);
+        x[r] = ok ? x[r] : fill;
+      }
+    }
+  }
+}
+
+template <bool KEYS_IN_ROWS>
+__device__ inline void mask_tile(f32x16& x, float fill, int route, bool causal, int Skv, int fixed_tok, TokMeta fixed,
+                                 int base, int hf, const int* meta_a, const int* meta_b, int moff) {
+  if (causal)
+    mask_tile_route<KEYS_IN_ROWS, true>(x, fill, route, Skv, fixed_tok, fixed, base, hf, meta_a, meta_b, moff);
+  else
+    mask_tile_route<KEYS_IN_ROWS, false>(x, fill, route, Skv, fixed_tok, fixed, base, hf, meta_a, meta_b, moff);
 }
 
 __device__ inline TokMeta q_meta(int route, const SegView& sv, int b, int Sq, int i) {

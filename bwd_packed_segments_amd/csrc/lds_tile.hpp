@@ -135,7 +135,44 @@ struct TileLoad {
   }
 };
 
+// The same tile through registers: load() issues the global loads (zeros for
+// rows from nvalid on), store() writes the swizzled chunks to LDS later, so
+// the loads overlap whatever runs in between.
+template <typename T, int ROWS, int D, int THREADS>
+struct TileRegs {
+  using F = TileFmt<T, D>;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  static constexpr int PER = ROWS * F::NC / THREADS;
+  static_assert((ROWS * F::NC) % THREADS == 0, "tile must split evenly over the workgroup");
+  u32x4v r[PER];
+
+  __device__ void load(const T* base, int64_t row_stride, int nvalid, int tid) {
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int s = x * THREADS + tid;
+      const int row = s / F::NC;
+      const int c = F::swz(row, s % F::NC);
+      r[x] = row < nvalid ? *reinterpret_cast<const u32x4v*>(base + row * row_stride + c * F::EPC)
+                          : u32x4v{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ void store(T* tile, int tid) const {
+#pragma unroll
+    for (int x = 0; x < PER; ++x) *reinterpret_cast<u32x4v*>(tile + (x * THREADS + tid) * F::EPC) = r[x];
+  }
+};
+
 // Waits for this thread's outstanding global->LDS loads.
 __device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Waits until at most N vector memory operations of this thread are
+// outstanding (they complete in issue order), leaving the N youngest in
+// flight.  gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 (set to their maximum, i.e. not waited for).
+template <int N>
+__device__ inline void wait_vm_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 }  // namespace bps
