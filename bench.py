@@ -41,7 +41,7 @@ PEAK_FP32_TFLOPS = 157.3
 METRIC = "fwd+bwd attention TFLOP/s (bf16) and % of MI355X MFMA peak, 1 GPU"
 DEFAULT_WORKLOAD = "gqa_causal_8k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["bps_common.hpp", "attn_kernels.hpp"]
+KERNEL_SOURCES = ["bps_common.hpp", "lds_tile.hpp", "attn_kernels.hpp", "attn_inst.hip"]
 
 
 # ------------------------------------------------------------------ counting
@@ -201,6 +201,21 @@ def cpu_baseline(w, case, n_alg_per_head_flops, budget_s=15.0):
             "seconds": t_total}
 
 
+# ------------------------------------------------------------------ counter calibration
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A device copy of known size: each launch reads and writes nbytes, so
+    the counters' per-dispatch readings for it give their scale factors."""
+    import torch
+    a = torch.ones(nbytes // 4, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": nbytes, "copy_bytes_written_per_launch": nbytes,
+                      "launches": reps}))
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -211,6 +226,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -225,6 +243,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     w = inputs.WORKLOADS[args.workload]
     t_setup = time.perf_counter()
