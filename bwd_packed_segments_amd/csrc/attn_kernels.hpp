@@ -846,7 +846,7 @@ struct DkvWsCfg {
   static constexpr int STAGE_BYTES = Q_BYTES + DO_BYTES + SIDE_BYTES;
   static constexpr int XSLOT_BYTES = 4 * 4 * 64 * 16;   // 4 key blocks x (P, P, dS, dS) x 64 lanes x 16 B
   static constexpr int LDS_BYTES = 3 * STAGE_BYTES + 2 * XSLOT_BYTES;
-  static constexpr bool ENABLED = sizeof(T) == 2 && DQK <= 128 && DV <= 128 && LDS_BYTES <= 160 * 1024;
+  static constexpr bool ENABLED = sizeof(T) == 2 && DQK <= 192 && DV <= 128 && LDS_BYTES <= 160 * 1024;
 };
 
 template <typename T, int DQK, int DV>
