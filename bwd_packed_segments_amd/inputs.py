@@ -66,6 +66,11 @@ WORKLOADS = {
     "gqa_causal_8k": Workload("gqa_causal_8k", 1, 8192, 8192, 64, 8, 128, 128, "bf16", True, "none"),
     "thd_cross_ring_4k": Workload("thd_cross_ring_4k", 1, 4096, 4096, 32, 8, 192, 128, "bf16", False,
                                   "cross_rotated", 256, 2048),
+    # One context-parallel shard of the long-sequence benchmark on the
+    # maxdiffusion ring-attention page (75,600 tokens, 40 heads, head dim
+    # 128, four shards): the local 18,900 queries against all 75,600 keys,
+    # non-causal, no padding mask.
+    "wan_cp_shard": Workload("wan_cp_shard", 1, 18900, 75600, 40, 40, 128, 128, "bf16", False, "none"),
 }
 
 # Order of the workloads as the benchmark contract lists them.

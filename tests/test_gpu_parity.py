@@ -177,3 +177,40 @@ def test_full_size_sampled_heads(name, heads):
     bench times; the oracle computes a sample of heads exactly."""
     case = inputs.make_case(name, 0)
     _parity(case, heads=heads)
+
+
+def test_long_shard_sampled_rows_and_sums():
+    """The long-sequence shard (18,900 queries x 75,600 keys, H=40, D=128,
+    non-causal) at full size.  Without a mask the query rows are
+    independent, so O, LSE and dQ of sampled rows are checked against the
+    oracle run on those rows alone (two heads); dK and dV are checked at
+    every key through identities that hold at any size: the keys' dV sum to
+    the queries' dO sum (softmax rows sum to one) and the keys' dK sum to
+    zero (each row of dS sums to zero)."""
+    import oracle
+    case = inputs.make_case("wan_cp_shard", 0)
+    w = case["workload"]
+    print(f"[parity] {w} sampled rows + sums", flush=True)
+    gpu = G.numpy_out(G.run_gpu(case))
+    rows = np.r_[0:16, 9000:9016, w.Sq - 16:w.Sq]
+    sub = dict(case)
+    sub["q"] = case["q"][:, rows]
+    sub["do"] = case["do"][:, rows]
+    heads = [0, 39]
+    ref = G.run_oracle(sub, heads=heads)
+    tol = G.TOL["bf16"]
+    for key in ("O", "dQ"):
+        g = gpu[key][:, rows][:, :, heads]
+        r = ref[key][:, :, heads]
+        assert np.all(np.abs(g - r) <= tol * np.maximum(1.0, np.abs(r))), key
+    g = gpu["LSE"][:, heads][:, :, rows]
+    r = ref["LSE"][:, heads]
+    assert np.all(np.abs(g - r) <= tol * np.maximum(1.0, np.abs(r))), "LSE"
+    # sums over all keys, every head
+    do_sum = case["do"].astype(np.float64).sum(axis=1)          # [B, H, Dv]
+    dv_sum = gpu["dV"].sum(axis=1)
+    scale = np.abs(gpu["dV"]).sum(axis=1) + 1.0
+    assert np.max(np.abs(dv_sum - do_sum) / scale) < 1e-2
+    dk_sum = gpu["dK"].sum(axis=1)
+    scale = np.abs(gpu["dK"]).sum(axis=1) + 1.0
+    assert np.max(np.abs(dk_sum) / scale) < 1e-2
