@@ -22,6 +22,8 @@ from .binding import (  # noqa: F401
     attn_bwd,
     attn_debug_mask,
     attn_fwd,
+    attn_ring_bwd,
+    attn_ring_fwd,
     bwd_workspace_size,
     fwd_workspace_size,
     lib,

@@ -28,7 +28,8 @@ STATUS_NAMES = {
 
 # Every symbol the header declares (the CPU tests check the library exports them).
 EXPORTS = ("attn_fwd_workspace_size", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_phase",
-           "attn_debug_mask", "attn_last_error", "attn_version")
+           "attn_debug_mask", "attn_ring_fwd_workspace_size", "attn_ring_bwd_workspace_size", "attn_ring_fwd",
+           "attn_ring_bwd", "attn_last_error", "attn_version")
 ATTN_BWD_PREPARE, ATTN_BWD_DKDV, ATTN_BWD_DQ, ATTN_BWD_ALL = 1, 2, 4, 7
 
 
@@ -92,6 +93,14 @@ def lib():
         L.attn_bwd_phase.restype = ctypes.c_int
         L.attn_debug_mask.argtypes = [dp, sp, vp, vp, vp, sz, vp]
         L.attn_debug_mask.restype = ctypes.c_int
+        L.attn_ring_fwd_workspace_size.argtypes = [dp, sp, ctypes.c_int32]
+        L.attn_ring_fwd_workspace_size.restype = sz
+        L.attn_ring_bwd_workspace_size.argtypes = [dp, sp, ctypes.c_int32]
+        L.attn_ring_bwd_workspace_size.restype = sz
+        L.attn_ring_fwd.argtypes = [dp, sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_ring_fwd.restype = ctypes.c_int
+        L.attn_ring_bwd.argtypes = [dp, sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_ring_bwd.restype = ctypes.c_int
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         L.attn_version.argtypes = []
@@ -321,6 +330,59 @@ def attn_debug_mask(*, B, Sq, Skv, causal=False, segments: Segments | None = Non
     _check(L.attn_debug_mask(ctypes.byref(desc), csp, mask.data_ptr(), routes.data_ptr(), ws.data_ptr(),
                              ws.numel(), _stream(torch.device(device))))
     return mask, routes
+
+
+def attn_ring_fwd(q, k, v, *, cp, causal=False, scale=None, segments: Segments | None = None, flags=0):
+    """O and LSE of fused attention computed as a one-GPU ring of cp shards
+    (attn_ring_fwd in the C ABI)."""
+    import torch
+    _require_device(q, k, v)
+    B, Sq, Hq, _ = q.shape
+    o = torch.empty((B, Sq, Hq, v.shape[3]), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
+    cs, csp = _seg_ptr(segments)
+    L = lib()
+    ws = _workspace(L.attn_ring_fwd_workspace_size(ctypes.byref(desc), csp, int(cp)), q.device)
+    _check(L.attn_ring_fwd(ctypes.byref(desc), csp, int(cp), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return o, lse
+
+
+def attn_ring_bwd(q, k, v, o, lse, do, *, cp, causal=False, scale=None, segments: Segments | None = None, flags=0):
+    """dQ, dK, dV computed as a one-GPU ring of cp shards (attn_ring_bwd)."""
+    import torch
+    _require_device(q, k, v, o, lse, do)
+    if do.stride() != o.stride() or do.shape != o.shape:
+        raise ValueError("dO must have the shape and strides of O")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    dq, dk, dv = (torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device) for t in (q, k, v))
+    desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
+    cs, csp = _seg_ptr(segments)
+    L = lib()
+    ws = _workspace(L.attn_ring_bwd_workspace_size(ctypes.byref(desc), csp, int(cp)), q.device)
+    _check(L.attn_ring_bwd(ctypes.byref(desc), csp, int(cp), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                           dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def ring_workspace_sizes(desc: attn_desc, segments: attn_segments | None, cp: int):
+    L = lib()
+    sp = ctypes.byref(segments) if segments else None
+    return (L.attn_ring_fwd_workspace_size(ctypes.byref(desc), sp, int(cp)),
+            L.attn_ring_bwd_workspace_size(ctypes.byref(desc), sp, int(cp)))
+
+
+def validate_ring_fwd(desc: attn_desc, segments: attn_segments | None, cp: int, *, ptr=1 << 12, ws=None,
+                      ws_bytes=0):
+    """attn_ring_fwd with placeholder addresses, for descriptors that must
+    fail host validation (nothing may launch); returns (status, message)."""
+    L = lib()
+    st = L.attn_ring_fwd(ctypes.byref(desc), ctypes.byref(segments) if segments else None, int(cp), ptr, ptr, ptr,
+                         ptr, ptr, ws, ws_bytes, None)
+    return st, L.attn_last_error().decode(errors="replace")
 
 
 def validate_fwd(desc: attn_desc, segments: attn_segments | None = None, *, q=1 << 12, k=1 << 12, v=1 << 12,

@@ -54,6 +54,7 @@ def common_flags():
 def units():
     out = []
     out.append(("seg_meta", [os.path.join(CSRC, "seg_meta.hip")], []))
+    out.append(("ring", [os.path.join(CSRC, "ring.hip")], []))
     out.append(("attn_api", ["-x", "hip", os.path.join(CSRC, "attn_api.cpp")], []))
     for t, dqk, dv in INSTANCES:
         for part, tag in ((0, "fwd"), (1, "dq"), (2, "dkdv")):

@@ -259,6 +259,121 @@ attn_status check_align(const char* name, const void* ptr, int dtype) {
   return ATTN_OK;
 }
 
+// ---------------------------------------------------------------- ring
+
+// Elements a [B, S, H, D] tensor with these strides spans (first to last
+// element), rounded up to 128 so consecutive partial copies stay aligned.
+size_t span_of(const attn_strides& st, int B, int S, int H, int D) {
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0) return 0;
+  const size_t n = (size_t)(B - 1) * st.batch + (size_t)(S - 1) * st.token + (size_t)(H - 1) * st.head + D;
+  return (n + 127) & ~static_cast<size_t>(127);
+}
+
+struct RingPlan {
+  int cp = 0, lq = 0, lkv = 0;
+  attn_desc sd{};              // descriptor of one (Q shard, KV shard) step
+  size_t esize = 0;
+  size_t span_q = 0, span_k = 0, span_v = 0, span_o = 0;
+  size_t off_ids_q = 0, off_pos_q = 0, off_ids_kv = 0, off_pos_kv = 0;
+  size_t off_lse = 0;          // fwd: partial LSEs; bwd: shard-major LSE
+  size_t off_p0 = 0;           // fwd: partial O; bwd: partial dQ
+  size_t off_p1 = 0, off_p2 = 0;   // bwd: partial dK, dV
+  size_t off_sub = 0, sub_bytes = 0;
+  size_t ws = 0;
+};
+
+attn_status make_ring_plan(const attn_desc* d, const attn_segments* seg, int cp, bool bwd, RingPlan* rp) {
+  Plan p;
+  attn_status st = make_plan(d, seg, &p);
+  if (st != ATTN_OK) return st;
+  if (cp < 1) return fail(ATTN_E_INVALID, "cp must be at least 1 (got %d)", cp);
+  if (d->Sq % cp || d->Skv % cp)
+    return fail(ATTN_E_INVALID, "Sq (%d) and Skv (%d) must be multiples of cp (%d)", d->Sq, d->Skv, cp);
+  rp->cp = cp;
+  rp->lq = d->Sq / cp;
+  rp->lkv = d->Skv / cp;
+  rp->sd = *d;
+  rp->sd.Sq = rp->lq;
+  rp->sd.Skv = rp->lkv;
+  rp->esize = d->dtype == ATTN_BF16 ? 2 : 4;
+  rp->span_q = span_of(d->q, d->B, d->Sq, d->Hq, d->Dqk);
+  rp->span_k = span_of(d->k, d->B, d->Skv, d->Hkv, d->Dqk);
+  rp->span_v = span_of(d->v, d->B, d->Skv, d->Hkv, d->Dv);
+  rp->span_o = span_of(d->o, d->B, d->Sq, d->Hq, d->Dv);
+  // Every step carries metadata in separate Q and KV buffers (sizes only
+  // depend on that, so placeholder pointers serve for the query).
+  attn_segments probe{reinterpret_cast<const int32_t*>(256), reinterpret_cast<const int32_t*>(512),
+                      reinterpret_cast<const int32_t*>(768), reinterpret_cast<const int32_t*>(1024)};
+  Plan sp;
+  if ((st = make_plan(&rp->sd, &probe, &sp)) != ATTN_OK) return st;
+  rp->sub_bytes = bwd ? sp.ws_bwd : sp.ws_fwd;
+  const size_t B = d->B;
+  size_t off = 0;
+  rp->off_ids_q = off; off = align_up(off + B * d->Sq * 4);
+  rp->off_pos_q = off; off = align_up(off + B * d->Sq * 4);
+  rp->off_ids_kv = off; off = align_up(off + B * d->Skv * 4);
+  rp->off_pos_kv = off; off = align_up(off + B * d->Skv * 4);
+  const size_t nlse = B * d->Hq * d->Sq;
+  if (!bwd) {
+    rp->off_lse = off; off = align_up(off + (size_t)cp * nlse * 4);
+    rp->off_p0 = off; off = align_up(off + (size_t)cp * rp->span_o * rp->esize);
+  } else {
+    rp->off_lse = off; off = align_up(off + nlse * 4);
+    rp->off_p0 = off; off = align_up(off + (size_t)cp * rp->span_q * rp->esize);
+    rp->off_p1 = off; off = align_up(off + (size_t)cp * rp->span_k * rp->esize);
+    rp->off_p2 = off; off = align_up(off + (size_t)cp * rp->span_v * rp->esize);
+  }
+  rp->off_sub = off; off = align_up(off + rp->sub_bytes);
+  rp->ws = off;
+  return ATTN_OK;
+}
+
+// Shard-major metadata of both sides in the workspace (global positions).
+attn_status ring_metadata(const attn_desc* d, const attn_segments* seg, const RingPlan& rp, char* ws,
+                          hipStream_t hs) {
+  bps::RingMetaArgs m{};
+  m.B = d->B; m.Sq = d->Sq; m.Skv = d->Skv; m.cp = rp.cp;
+  if (seg) {
+    const bool self = seg->ids_kv == nullptr;
+    m.ids[0] = seg->ids_q;
+    m.pos[0] = seg->pos_q;
+    m.ids[1] = self ? seg->ids_q : seg->ids_kv;
+    m.pos[1] = self ? seg->pos_q : seg->pos_kv;
+  }
+  m.ids_out[0] = reinterpret_cast<int*>(ws + rp.off_ids_q);
+  m.pos_out[0] = reinterpret_cast<int*>(ws + rp.off_pos_q);
+  m.ids_out[1] = reinterpret_cast<int*>(ws + rp.off_ids_kv);
+  m.pos_out[1] = reinterpret_cast<int*>(ws + rp.off_pos_kv);
+  hipError_t e = bps::launch_ring_meta(m, hs);
+  if (e != hipSuccess) return fail(ATTN_E_DEVICE, "ring metadata kernel: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+// Step (rank r, ring step t): Q shard r against KV shard (r - t) mod cp.
+struct RingStep {
+  attn_desc d;
+  attn_segments seg;
+  int s;
+};
+
+RingStep ring_step(const RingPlan& rp, int B, char* ws, int r, int t) {
+  RingStep x;
+  x.d = rp.sd;
+  if (t > 0) x.d.flags |= ATTN_FORCE_GENERAL;   // rotated steps: general route
+  x.s = (r - t + rp.cp) % rp.cp;
+  const size_t oq = (size_t)r * B * rp.lq, okv = (size_t)x.s * B * rp.lkv;
+  x.seg.ids_q = reinterpret_cast<const int32_t*>(ws + rp.off_ids_q) + oq;
+  x.seg.pos_q = reinterpret_cast<const int32_t*>(ws + rp.off_pos_q) + oq;
+  x.seg.ids_kv = reinterpret_cast<const int32_t*>(ws + rp.off_ids_kv) + okv;
+  x.seg.pos_kv = reinterpret_cast<const int32_t*>(ws + rp.off_pos_kv) + okv;
+  return x;
+}
+
+const char* cadd(const void* base, size_t elems, size_t esize) {
+  return static_cast<const char*>(base) + elems * esize;
+}
+char* madd(void* base, size_t elems, size_t esize) { return static_cast<char*>(base) + elems * esize; }
+
 }  // namespace
 
 extern "C" {
@@ -373,6 +488,119 @@ attn_status attn_debug_mask(const attn_desc* d, const attn_segments* seg, uint8_
     if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg)) != ATTN_OK) return st;
     hipError_t e = bps::launch_debug_mask(a, hs);
     if (e != hipSuccess) return fail(ATTN_E_DEVICE, "mask launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
+}
+
+size_t attn_ring_fwd_workspace_size(const attn_desc* desc, const attn_segments* seg, int32_t cp) {
+  RingPlan rp;
+  return make_ring_plan(desc, seg, cp, false, &rp) == ATTN_OK ? rp.ws : 0;
+}
+
+size_t attn_ring_bwd_workspace_size(const attn_desc* desc, const attn_segments* seg, int32_t cp) {
+  RingPlan rp;
+  return make_ring_plan(desc, seg, cp, true, &rp) == ATTN_OK ? rp.ws : 0;
+}
+
+attn_status attn_ring_fwd(const attn_desc* d, const attn_segments* seg, int32_t cp, const void* q, const void* k,
+                          const void* v, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  try {
+    RingPlan rp;
+    attn_status st = make_ring_plan(d, seg, cp, false, &rp);
+    if (st != ATTN_OK) return st;
+    const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
+    if (need_nonnull(q, nq) || need_nonnull(o, nq) || need_nonnull(lse, nq))
+      return fail(ATTN_E_INVALID, "q, o and lse must not be NULL");
+    if (need_nonnull(k, nkv) || need_nonnull(v, nkv)) return fail(ATTN_E_INVALID, "k and v must not be NULL");
+    if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
+        (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)))
+      return st;
+    if ((st = check_ws(workspace, workspace_bytes, rp.ws)) != ATTN_OK) return st;
+    if (d->Sq == 0) return ATTN_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    if ((st = ring_metadata(d, seg, rp, ws, hs)) != ATTN_OK) return st;
+    const size_t es = rp.esize;
+    float* lse_parts = reinterpret_cast<float*>(ws + rp.off_lse);
+    const size_t nl = (size_t)d->B * d->Hq * rp.lq;
+    for (int t = 0; t < cp; ++t)
+      for (int r = 0; r < cp; ++r) {
+        const RingStep x = ring_step(rp, d->B, ws, r, t);
+        const size_t rq = (size_t)r * rp.lq, rkv = (size_t)x.s * rp.lkv;
+        st = attn_fwd(&x.d, &x.seg, cadd(q, rq * d->q.token, es), cadd(k, rkv * d->k.token, es),
+                      cadd(v, rkv * d->v.token, es), madd(ws + rp.off_p0, t * rp.span_o + rq * d->o.token, es),
+                      lse_parts + ((size_t)t * cp + r) * nl, ws + rp.off_sub, rp.sub_bytes, stream, nullptr);
+        if (st != ATTN_OK) return st;
+      }
+    bps::RingMergeArgs m{};
+    m.B = d->B; m.Sq = d->Sq; m.Hq = d->Hq; m.Dv = d->Dv; m.cp = cp;
+    m.o_parts = ws + rp.off_p0;
+    m.part_elems = rp.span_o;
+    m.lse_parts = lse_parts;
+    m.o = o; m.lse = lse;
+    m.so = strides_of(d->o);
+    hipError_t e = bps::launch_ring_merge(d->dtype == ATTN_BF16, m, hs);
+    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "ring merge: %s", hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
+}
+
+attn_status attn_ring_bwd(const attn_desc* d, const attn_segments* seg, int32_t cp, const void* q, const void* k,
+                          const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                          void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    RingPlan rp;
+    attn_status st = make_ring_plan(d, seg, cp, true, &rp);
+    if (st != ATTN_OK) return st;
+    const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
+    if (need_nonnull(q, nq) || need_nonnull(o, nq) || need_nonnull(lse, nq) || need_nonnull(dout, nq) ||
+        need_nonnull(dq, nq))
+      return fail(ATTN_E_INVALID, "q, o, lse, dout and dq must not be NULL");
+    if (need_nonnull(k, nkv) || need_nonnull(v, nkv) || need_nonnull(dk, nkv) || need_nonnull(dv, nkv))
+      return fail(ATTN_E_INVALID, "k, v, dk and dv must not be NULL");
+    if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
+        (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)) ||
+        (st = check_align("dout", dout, d->dtype)) || (st = check_align("dq", dq, d->dtype)) ||
+        (st = check_align("dk", dk, d->dtype)) || (st = check_align("dv", dv, d->dtype)))
+      return st;
+    if ((st = check_ws(workspace, workspace_bytes, rp.ws)) != ATTN_OK) return st;
+    if (d->Sq == 0 && d->Skv == 0) return ATTN_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    if ((st = ring_metadata(d, seg, rp, ws, hs)) != ATTN_OK) return st;
+    float* lse_sh = reinterpret_cast<float*>(ws + rp.off_lse);
+    bps::RingLseArgs la{d->B, d->Hq, d->Sq, cp, lse, lse_sh};
+    hipError_t e = bps::launch_ring_lse_shards(la, hs);
+    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "ring LSE shards: %s", hipGetErrorString(e));
+    const size_t es = rp.esize;
+    const size_t nl = (size_t)d->B * d->Hq * rp.lq;
+    for (int t = 0; t < cp; ++t)
+      for (int r = 0; r < cp; ++r) {
+        const RingStep x = ring_step(rp, d->B, ws, r, t);
+        const size_t rq = (size_t)r * rp.lq, rkv = (size_t)x.s * rp.lkv;
+        st = attn_bwd(&x.d, &x.seg, cadd(q, rq * d->q.token, es), cadd(k, rkv * d->k.token, es),
+                      cadd(v, rkv * d->v.token, es), cadd(o, rq * d->o.token, es), lse_sh + (size_t)r * nl,
+                      cadd(dout, rq * d->o.token, es), madd(ws + rp.off_p0, t * rp.span_q + rq * d->q.token, es),
+                      madd(ws + rp.off_p1, t * rp.span_k + rkv * d->k.token, es),
+                      madd(ws + rp.off_p2, t * rp.span_v + rkv * d->v.token, es), ws + rp.off_sub, rp.sub_bytes,
+                      stream, nullptr);
+        if (st != ATTN_OK) return st;
+      }
+    const int bf = d->dtype == ATTN_BF16;
+    bps::RingReduceArgs ra{d->B, d->Sq, d->Hq, d->Dqk, cp, ws + rp.off_p0, rp.span_q, dq, strides_of(d->q)};
+    if ((e = bps::launch_ring_reduce(bf, ra, hs)) != hipSuccess)
+      return fail(ATTN_E_DEVICE, "ring reduce dq: %s", hipGetErrorString(e));
+    ra = bps::RingReduceArgs{d->B, d->Skv, d->Hkv, d->Dqk, cp, ws + rp.off_p1, rp.span_k, dk, strides_of(d->k)};
+    if ((e = bps::launch_ring_reduce(bf, ra, hs)) != hipSuccess)
+      return fail(ATTN_E_DEVICE, "ring reduce dk: %s", hipGetErrorString(e));
+    ra = bps::RingReduceArgs{d->B, d->Skv, d->Hkv, d->Dv, cp, ws + rp.off_p2, rp.span_v, dv, strides_of(d->v)};
+    if ((e = bps::launch_ring_reduce(bf, ra, hs)) != hipSuccess)
+      return fail(ATTN_E_DEVICE, "ring reduce dv: %s", hipGetErrorString(e));
     return ATTN_OK;
   } catch (...) {
     return fail(ATTN_E_DEVICE, "unexpected host exception");

@@ -71,6 +71,44 @@ struct MaskArgs {
   int* route_rows;  // [B] or NULL
 };
 
+// One-GPU ring emulation (ring.hip).
+struct RingMetaArgs {
+  int B, Sq, Skv, cp;
+  const int* ids[2];   // source [B, S] per side (Q, KV); NULL: id 1, position = index
+  const int* pos[2];   // NULL with ids given: derived on the whole row
+  int* ids_out[2];     // [cp][B][S / cp]
+  int* pos_out[2];
+};
+
+struct RingLseArgs {
+  int B, Hq, Sq, cp;
+  const float* lse;    // [B, Hq, Sq]
+  float* lse_out;      // [cp][B][Hq][Sq / cp]
+};
+
+struct RingMergeArgs {
+  int B, Sq, Hq, Dv, cp;
+  const void* o_parts;      // cp partial outputs with the layout of o
+  size_t part_elems;        // elements between consecutive partials
+  const float* lse_parts;   // [t][rank][B][Hq][Sq / cp]
+  void* o;
+  float* lse;               // [B, Hq, Sq]
+  Strides so;
+};
+
+struct RingReduceArgs {
+  int B, S, H, D, nparts;
+  const void* parts;        // nparts partials with the layout of out
+  size_t part_elems;
+  void* out;
+  Strides st;
+};
+
+hipError_t launch_ring_meta(const RingMetaArgs& a, hipStream_t st);
+hipError_t launch_ring_lse_shards(const RingLseArgs& a, hipStream_t st);
+hipError_t launch_ring_merge(int dtype_bf16, const RingMergeArgs& a, hipStream_t st);
+hipError_t launch_ring_reduce(int dtype_bf16, const RingReduceArgs& a, hipStream_t st);
+
 // Launchers (defined in the kernel translation units).  Each returns the
 // result of hipGetLastError() after its launches.
 hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st);

@@ -183,6 +183,46 @@ attn_status attn_debug_mask(const attn_desc* desc, const attn_segments* seg,
                             uint8_t* mask_out, int32_t* route_rows,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* One-GPU emulation of ring (context-parallel) attention, the long-sequence
+ * scheme of the maxdiffusion ring-attention backward page (Summary and Key
+ * Features: K, V, dK and dV rotate between devices while each device keeps
+ * its queries and accumulates dQ).  Q is cut into cp shards of Sq / cp
+ * tokens and KV into cp shards of Skv / cp tokens (both must divide).  At
+ * ring step t the emulated device r holds Q shard r and KV shard
+ * (r - t) mod cp and runs the fused attention on that pair; steps t > 0 are
+ * forced onto the general metadata route, as the TransformerEngine page on
+ * fused attention sharding does for rotated ring steps (Changes 3).
+ *
+ * Segment metadata are those of the whole sequence, as for attn_fwd:
+ * positions (given or derived from the ids on the whole row) stay global,
+ * so a segment cut by a shard boundary keeps its mask.  Without metadata
+ * every token gets id 1 and its index as position, which reproduces the
+ * plain or index-causal mask.
+ *
+ * attn_ring_fwd: per step an output and LSE for the step's keys, merged
+ * into O and LSE by log-sum-exp in fp32 (a row no step attends: O = 0,
+ * LSE = -inf).  attn_ring_bwd: per step the gradients against the merged O
+ * and LSE, which are exact partial sums; dQ of a Q shard and dK, dV of a KV
+ * shard are the sums of their step partials, taken in step order in fp32,
+ * so the result is deterministic.  Both equal attn_fwd / attn_bwd on the
+ * whole sequence up to rounding (each partial is rounded to the tensor
+ * dtype once).  Tensors, strides, ownership and errors as for attn_fwd and
+ * attn_bwd; cp < 1 or a shard size that does not divide is ATTN_E_INVALID.
+ * The workspace holds the shard-major metadata, the step partials (cp
+ * copies of O, or of dQ, dK and dV, each as large as the tensor's extent)
+ * and one step's attention workspace; its contents are dead after the call. */
+size_t attn_ring_fwd_workspace_size(const attn_desc* desc, const attn_segments* seg, int32_t cp);
+size_t attn_ring_bwd_workspace_size(const attn_desc* desc, const attn_segments* seg, int32_t cp);
+attn_status attn_ring_fwd(const attn_desc* desc, const attn_segments* seg, int32_t cp,
+                          const void* q, const void* k, const void* v,
+                          void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_ring_bwd(const attn_desc* desc, const attn_segments* seg, int32_t cp,
+                          const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout,
+                          void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* attn_last_error(void);
 

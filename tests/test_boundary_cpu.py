@@ -151,3 +151,31 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="no fallback"):
         B.lib()
     monkeypatch.setattr(B, "_lib", None)
+
+
+def test_ring_validation():
+    d = good(Sq=300, Skv=300)
+    st, text = B.validate_ring_fwd(d, None, 0)
+    assert st == B.ATTN_E_INVALID and "cp" in text
+    st, text = B.validate_ring_fwd(d, None, 7)
+    assert st == B.ATTN_E_INVALID and "multiples of cp" in text
+    st, text = B.validate_ring_fwd(good(Hq=6, Hkv=4), None, 2)        # descriptor errors come first
+    assert st == B.ATTN_E_INVALID and "multiple" in text
+    st, text = B.validate_ring_fwd(good(Skv=200), None, 2)            # causal without metadata needs Sq == Skv
+    assert st == B.ATTN_E_UNSUPPORTED
+    fwd, bwd = B.ring_workspace_sizes(d, None, 3)
+    st, text = B.validate_ring_fwd(d, None, 3, ws=1 << 20, ws_bytes=fwd - 1)
+    assert st == B.ATTN_E_WORKSPACE and "smaller" in text
+
+
+def test_ring_workspace_sizes():
+    d = good(Sq=600, Skv=600)
+    f1, b1 = B.ring_workspace_sizes(d, None, 1)
+    f3, b3 = B.ring_workspace_sizes(d, None, 3)
+    assert f1 > 0 and b1 > 0
+    # cp partial copies of O (forward) or of dQ, dK, dV (backward)
+    o_bytes = 2 * 600 * 4 * 128 * 2
+    qkv_bytes = (2 * 600 * 4 * 128 + 2 * 2 * 600 * 2 * 128) * 2
+    assert f1 >= o_bytes and f3 >= 3 * o_bytes
+    assert b1 >= qkv_bytes and b3 >= 3 * qkv_bytes
+    assert B.ring_workspace_sizes(d, None, 7) == (0, 0)
