@@ -170,6 +170,48 @@ def run_gpu(w, steps, warmup, seed=0):
     return case, wall, avg, med, fwd.route
 
 
+def ring_bench(w, cp, steps, warmup, seed=0):
+    """One JSON line for the ring emulation: algorithmic FLOP of the whole
+    sequence over the time of attn_ring_fwd + attn_ring_bwd (cp x cp shard
+    steps, the log-sum-exp merge and the gradient sums)."""
+    import torch
+    import bwd_packed_segments_amd as bps
+    case = inputs.make_case(w, seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = {k: torch.from_numpy(case[k]).to("cuda").to(dt) for k in ("q", "k", "v", "do")}
+    seg = None
+    if case["segments"] is not None:
+        sg = case["segments"]
+
+        def t(x):
+            return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
+        seg = bps.Segments(t(sg["ids_q"]), t(sg.get("pos_q")), t(sg.get("ids_kv")), t(sg.get("pos_kv")))
+
+    def step():
+        o, lse = bps.attn_ring_fwd(dev["q"], dev["k"], dev["v"], cp=cp, causal=w.causal, segments=seg)
+        bps.attn_ring_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], cp=cp, causal=w.causal, segments=seg)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    n = allowed_pairs(w, case["segments"])
+    F = flops(w, n)
+    f_step = F["fwd"] + F["bwd"]
+    value = f_step / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    print(json.dumps({"metric": METRIC + " (one-GPU ring emulation)", "value": round(value, 2), "unit": "TFLOP/s",
+                      "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+                      "data": f"synthetic (seeded iid N(0,1) tensors, seed {seed})",
+                      "config": {"workload": w.name, "ring_shards": cp, "allowed_pairs": n, "flop_per_step": f_step},
+                      "pct_peak": round(100.0 * value / peak, 2)}))
+
+
 # ------------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(w, case, n_alg_per_head_flops, budget_s=15.0):
@@ -237,6 +279,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--ring", type=int, default=0, metavar="CP",
+                    help="time the one-GPU ring emulation with CP shards (attn_ring_fwd + attn_ring_bwd) "
+                         "instead of the plain entry points; same workload and FLOP count")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -261,6 +306,9 @@ def main():
 
     w = inputs.WORKLOADS[args.workload]
     t_setup = time.perf_counter()
+    if args.ring:
+        ring_bench(w, args.ring, args.steps, args.warmup)
+        return
     case, wall, avg, med, route = run_gpu(w, args.steps, args.warmup)
     n = allowed_pairs(w, case["segments"])
     F = flops(w, n)

@@ -77,6 +77,20 @@ __device__ inline void q_range(int route, bool causal, int Sq, int k0, int nk, c
   if (hi < lo) hi = lo;
 }
 
+// Tile classes of a workgroup's walk, kept in LDS.  On the metadata routes
+// classifying a tile reads the 32-token summaries from global memory, a
+// round trip the loop would otherwise wait for on every step; instead the
+// workgroup classifies the first kClassCap tiles of its walk at once (each
+// thread a few, one round trip in all).  Tiles past the table (very long
+// walks) are classified when reached.
+constexpr int kClassCap = 1024;
+
+template <typename F>
+__device__ inline void fill_classes(unsigned char* tab, int n, int tid, int nthreads, F classify_walk) {
+  const int m = min(n, kClassCap);
+  for (int i = tid; i < m; i += nthreads) tab[i] = static_cast<unsigned char>(classify_walk(i));
+}
+
 // LDS staging: two buffers when two workgroups with two buffers fit in the
 // 160 KB of a CU, otherwise one; two waves per SIMD when two workgroups fit.
 template <typename T, int STAGE>
@@ -176,9 +190,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
     if (route != kRouteDense) ks = tile_sum(sum_kv_row, a.seg.nch_kv, kt * BN, BN);
     return classify_tile(route, causal, s.Skv, q0, BM, kt * BN, BN, qs, ks);
   };
+  __shared__ unsigned char cls_tab[kClassCap];
+  const bool tabled = route != kRouteDense;
+  if (tabled) {
+    fill_classes(cls_tab, t_hi - t_lo, tid, 256, [&](int i) { return classify(t_lo + i); });
+    __syncthreads();
+  }
   auto next_tile = [&](int kt, int& cls) -> int {
     for (int k = kt; k < t_hi; ++k) {
-      cls = classify(k);
+      cls = (tabled && k - t_lo < kClassCap) ? (int)cls_tab[k - t_lo] : classify(k);
       if (cls != kTileSkip) return k;
     }
     cls = kTileSkip;
@@ -430,9 +450,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<
     if (route != kRouteDense) ks = tile_sum(sum_kv_row, a.seg.nch_kv, kt * BN, BN);
     return classify_tile(route, causal, s.Skv, q0, BM, kt * BN, BN, qs, ks);
   };
+  __shared__ unsigned char cls_tab[kClassCap];
+  const bool tabled = route != kRouteDense;
+  if (tabled) {
+    fill_classes(cls_tab, t_hi - t_lo, tid, 256, [&](int i) { return classify(t_lo + i); });
+    __syncthreads();
+  }
   auto next_tile = [&](int kt, int& cls) -> int {
     for (int k = kt; k < t_hi; ++k) {
-      cls = classify(k);
+      cls = (tabled && k - t_lo < kClassCap) ? (int)cls_tab[k - t_lo] : classify(k);
       if (cls != kTileSkip) return k;
     }
     cls = kTileSkip;
@@ -611,11 +637,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
     if (route != kRouteDense) qs = tile_sum(sum_q_row, a.seg.nch_q, qt * BM, BM);
     return classify_tile(route, causal, s.Skv, qt * BM, BM, k0, BN, qs, ks);
   };
+  __shared__ unsigned char cls_tab[kClassCap];
+  const bool tabled = route != kRouteDense;
+  if (tabled) {
+    fill_classes(cls_tab, ntiles, tid, 256, [&](int u) { return classify(t_hi - 1 - u); });
+    __syncthreads();
+  }
   auto next_step = [&](int x, int& cls) -> int {
     while (x < nsteps) {
-      cls = classify(tile_of(x));
+      const int u = x / g;
+      cls = (tabled && u < kClassCap) ? (int)cls_tab[u] : classify(tile_of(x));
       if (cls != kTileSkip) return x;
-      x = (x / g + 1) * g;   // the whole tile is skipped for every head
+      x = (u + 1) * g;   // the whole tile is skipped for every head
     }
     cls = kTileSkip;
     return nsteps;
@@ -900,11 +933,18 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     if (route != kRouteDense) qs = tile_sum(sum_q_row, a.seg.nch_q, qt * BM, BM);
     return classify_tile(route, causal, s.Skv, qt * BM, BM, k0, BN, qs, ks);
   };
+  __shared__ unsigned char cls_tab[kClassCap];
+  const bool tabled = route != kRouteDense;
+  if (tabled) {
+    fill_classes(cls_tab, ntiles, tid, C::THREADS, [&](int u) { return classify(t_hi - 1 - u); });
+    __syncthreads();
+  }
   auto next_step = [&](int x, int& cls) -> int {
     while (x < nsteps) {
-      cls = classify(tile_of(x));
+      const int u = x / g;
+      cls = (tabled && u < kClassCap) ? (int)cls_tab[u] : classify(tile_of(x));
       if (cls != kTileSkip) return x;
-      x = (x / g + 1) * g;
+      x = (u + 1) * g;
     }
     cls = kTileSkip;
     return nsteps;

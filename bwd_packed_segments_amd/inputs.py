@@ -71,6 +71,9 @@ WORKLOADS = {
     # 128, four shards): the local 18,900 queries against all 75,600 keys,
     # non-causal, no padding mask.
     "wan_cp_shard": Workload("wan_cp_shard", 1, 18900, 75600, 40, 40, 128, 128, "bf16", False, "none"),
+    # The whole 75,600-token sequence of that benchmark (for the one-GPU
+    # ring emulation with four shards of 18,900 tokens).
+    "wan_full_76k": Workload("wan_full_76k", 1, 75600, 75600, 40, 40, 128, 128, "bf16", False, "none"),
 }
 
 # Order of the workloads as the benchmark contract lists them.
