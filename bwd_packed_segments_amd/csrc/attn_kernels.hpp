@@ -1106,6 +1106,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int kBatch = TileLoad<T, BM, DQK, 256>::PER + TileLoad<T, BM, DV, 256>::PER;
 
   if (producer) {
+    // The producers' chain (products, exponentials, dS) is the critical path
+    // of a phase; at a higher wave priority their instructions win issue
+    // over the consumers' when both are ready on a SIMD (measured: 7-8 %
+    // less time than equal priorities on the 8K causal GQA workload).
+    __builtin_amdgcn_s_setprio(3);
     Sched t = sched_init();
     if (t.x < nsteps) issue(t.x, smem);
     if (t.nx < nsteps) issue(t.nx, smem + C::STAGE_BYTES);
