@@ -269,6 +269,47 @@ def copy_calibration(nbytes=1 << 30, reps=3):
                       "launches": reps}))
 
 
+def ingest_counters(d, workload):
+    """Writes the HBM-traffic record bench reports from four rocprofv3
+    counter runs in directory d: C (FETCH_SIZE) and D (WRITE_SIZE) over a
+    bench run of the workload, copyC / copyD the same counters over
+    --copy-calibration.  Readings are KiB per dispatch; each counter's factor
+    is the copy's true bytes over what the counter read for it."""
+    import csv
+    import re
+
+    def per_kernel(tag):
+        out = {}
+        with open(os.path.join(d, f"{tag}_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                m = re.search(r"(attn_[a-z_]+?)(?:_ws)?_kernel", r["Kernel_Name"])
+                name = m.group(1) if m else ("copy" if "copy" in r["Kernel_Name"] else None)
+                if name:
+                    out.setdefault(name, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    copy_bytes = 1 << 30
+    cf, cw = per_kernel("copyC")["copy"], per_kernel("copyD")["copy"]
+    fetch_factor, write_factor = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    rec = {"_comment": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
+                       "each scaled by what it read for a 1 GiB device copy; source_hash is "
+                       "kernel_source_hash() of the sources the counters were taken on",
+           "calibration": {"copy_bytes": copy_bytes, "fetch_kib_read": round(cf), "write_kib_read": round(cw),
+                           "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)}}
+    fetch, write = per_kernel("C"), per_kernel("D")
+    h = kernel_source_hash()
+    for k in sorted(fetch):
+        if k == "copy" or k not in write:
+            continue
+        fb, wb = fetch[k] * 1024 * fetch_factor, write[k] * 1024 * write_factor
+        rec[f"{k}:{workload}"] = {"source_hash": h, "fetch_bytes": int(fb), "write_bytes": int(wb),
+                                  "bytes_per_launch": int(fb + wb)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -285,8 +326,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
+    ap.add_argument("--ingest-counters", metavar="DIR",
+                    help="no GPU work: read rocprofv3 FETCH_SIZE / WRITE_SIZE runs (C, D, copyC, copyD "
+                         "counter_collection.csv in DIR) for --workload and write the traffic record")
     args = ap.parse_args()
 
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no multi-GPU path. "
               "Run with --gpus 1.", file=sys.stderr)
