@@ -25,9 +25,15 @@ attention and its analytic gradient, written out with dense matrices, one
   (TransformerEngine PR 2358): separate qk and v head dims (review of the
   KV-packed stride); zeroed gradients for ragged layouts (Greptile Overview).
 
-Every function here has a pin in ``tests/test_oracle_pins.py`` that ties it
-to something other than itself (finite differences, closed forms, a library
-routine for the special cases it reduces to, brute force on tiny inputs).
+``variants.py`` adds the attention variants the TransformerEngine pages
+name without defining (additive bias and its gradient, score modification
+by soft-capping, a sink logit and its gradient, the per-head maximum logit);
+its readings are stated in its docstring.
+
+Every function here has a pin in ``tests/test_oracle_pins.py`` or
+``tests/test_oracle_variant_pins.py`` that ties it to something other than
+itself (finite differences, closed forms, a library routine for the special
+cases it reduces to, brute force on tiny inputs).
 """
 
 from .attention import (  # noqa: F401
@@ -39,3 +45,4 @@ from .attention import (  # noqa: F401
     kv_head_of,
     resolve_segments,
 )
+from .variants import backward_ex, forward_ex  # noqa: F401,E402
