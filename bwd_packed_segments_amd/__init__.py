@@ -20,8 +20,10 @@ from .binding import (  # noqa: F401
     FwdPlan,
     Segments,
     attn_bwd,
+    attn_bwd_ex,
     attn_debug_mask,
     attn_fwd,
+    attn_fwd_ex,
     attn_ring_bwd,
     attn_ring_fwd,
     bwd_workspace_size,

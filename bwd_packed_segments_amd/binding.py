@@ -29,7 +29,8 @@ STATUS_NAMES = {
 # Every symbol the header declares (the CPU tests check the library exports them).
 EXPORTS = ("attn_fwd_workspace_size", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_phase",
            "attn_debug_mask", "attn_ring_fwd_workspace_size", "attn_ring_bwd_workspace_size", "attn_ring_fwd",
-           "attn_ring_bwd", "attn_last_error", "attn_version")
+           "attn_ring_bwd", "attn_fwd_ex_workspace_size", "attn_bwd_ex_workspace_size", "attn_fwd_ex",
+           "attn_bwd_ex", "attn_bwd_ex_phase", "attn_last_error", "attn_version")
 ATTN_BWD_PREPARE, ATTN_BWD_DKDV, ATTN_BWD_DQ, ATTN_BWD_ALL = 1, 2, 4, 7
 
 
@@ -57,6 +58,12 @@ class attn_desc(ctypes.Structure):
 class attn_segments(ctypes.Structure):
     _fields_ = [("ids_q", ctypes.c_void_p), ("pos_q", ctypes.c_void_p),
                 ("ids_kv", ctypes.c_void_p), ("pos_kv", ctypes.c_void_p)]
+
+
+class attn_variant(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("bias_batch", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("sink", ctypes.c_void_p), ("max_logit", ctypes.c_void_p), ("dbias", ctypes.c_void_p),
+                ("dsink", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -101,6 +108,18 @@ def lib():
         L.attn_ring_fwd.restype = ctypes.c_int
         L.attn_ring_bwd.argtypes = [dp, sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_ring_bwd.restype = ctypes.c_int
+        varp = ctypes.POINTER(attn_variant)
+        L.attn_fwd_ex_workspace_size.argtypes = [dp, sp, varp]
+        L.attn_fwd_ex_workspace_size.restype = sz
+        L.attn_bwd_ex_workspace_size.argtypes = [dp, sp, varp]
+        L.attn_bwd_ex_workspace_size.restype = sz
+        L.attn_fwd_ex.argtypes = [dp, sp, varp, vp, vp, vp, vp, vp, vp, sz, vp, i32p]
+        L.attn_fwd_ex.restype = ctypes.c_int
+        L.attn_bwd_ex.argtypes = [dp, sp, varp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i32p]
+        L.attn_bwd_ex.restype = ctypes.c_int
+        L.attn_bwd_ex_phase.argtypes = [ctypes.c_int32, dp, sp, varp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                        vp, i32p]
+        L.attn_bwd_ex_phase.restype = ctypes.c_int
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         L.attn_version.argtypes = []
@@ -404,3 +423,98 @@ def validate_bwd(desc: attn_desc, segments: attn_segments | None = None, *, ptr=
     st = L.attn_bwd(ctypes.byref(desc), ctypes.byref(segments) if segments else None, ptr, ptr, ptr, ptr, ptr,
                     ptr, dqp, ptr, ptr, ws, ws_bytes, None, None)
     return st, L.attn_last_error().decode(errors="replace")
+
+
+# ------------------------------------------------------------------ variants
+
+def _variant(q, bias, softcap, sink, max_logit=None, dbias=None, dsink=None):
+    """attn_variant for device tensors (None fields stay NULL)."""
+    import torch
+    B, Sq, Hq, _ = q.shape
+    bias_batch = 1
+    if bias is not None:
+        _require_device(bias)
+        if bias.dtype != q.dtype or not bias.is_contiguous() or bias.dim() != 4 or bias.shape[1] != Hq \
+                or bias.shape[2] != Sq or bias.shape[0] not in (1, B):
+            raise ValueError("bias must be a contiguous [1 or B, Hq, Sq, Skv] tensor of q's dtype")
+        bias_batch = bias.shape[0]
+    if sink is not None:
+        _require_device(sink)
+        if sink.dtype != torch.float32 or not sink.is_contiguous() or tuple(sink.shape) != (Hq,):
+            raise ValueError("sink must be a contiguous float32 [Hq] tensor")
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+    return attn_variant(ptr(bias), bias_batch, float(softcap or 0.0), ptr(sink), ptr(max_logit), ptr(dbias),
+                        ptr(dsink))
+
+
+def attn_fwd_ex(q, k, v, *, causal=False, scale=None, segments: Segments | None = None, flags=0, bias=None,
+                softcap=0.0, sink=None, return_max_logit=False):
+    """O, LSE (and the per-head max logit when asked) of fused attention with
+    an additive bias [1 or B, Hq, Sq, Skv], soft-capping and sink logits
+    [Hq] (attn_fwd_ex in the C ABI)."""
+    import torch
+    _require_device(q, k, v)
+    B, Sq, Hq, _ = q.shape
+    o = torch.empty((B, Sq, Hq, v.shape[3]), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    ml = torch.empty((Hq,), dtype=torch.float32, device=q.device) if return_max_logit else None
+    desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
+    var = _variant(q, bias, softcap, sink, max_logit=ml)
+    cs, csp = _seg_ptr(segments)
+    L = lib()
+    ws = _workspace(L.attn_fwd_ex_workspace_size(ctypes.byref(desc), csp, ctypes.byref(var)), q.device)
+    _check(L.attn_fwd_ex(ctypes.byref(desc), csp, ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device), None))
+    return (o, lse, ml) if return_max_logit else (o, lse)
+
+
+def attn_bwd_ex(q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segments | None = None, flags=0,
+                bias=None, softcap=0.0, sink=None, need_dbias=True, need_dsink=True):
+    """dQ, dK, dV, dbias (None without bias or when not needed) and dsink
+    (None without sink or when not needed) of fused attention with the
+    variants of attn_fwd_ex (attn_bwd_ex in the C ABI)."""
+    import torch
+    _require_device(q, k, v, o, lse, do)
+    if do.stride() != o.stride() or do.shape != o.shape:
+        raise ValueError("dO must have the shape and strides of O")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    dq, dk, dv = (torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device) for t in (q, k, v))
+    dbias = torch.empty_like(bias) if (bias is not None and need_dbias) else None
+    dsink = torch.empty((q.shape[2],), dtype=torch.float32, device=q.device) \
+        if (sink is not None and need_dsink) else None
+    desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
+    var = _variant(q, bias, softcap, sink, dbias=dbias, dsink=dsink)
+    cs, csp = _seg_ptr(segments)
+    L = lib()
+    ws = _workspace(L.attn_bwd_ex_workspace_size(ctypes.byref(desc), csp, ctypes.byref(var)), q.device)
+    _check(L.attn_bwd_ex(ctypes.byref(desc), csp, ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         ws.data_ptr(), ws.numel(), _stream(q.device), None))
+    return dq, dk, dv, dbias, dsink
+
+
+def validate_ex(desc: attn_desc, var: attn_variant, segments: attn_segments | None = None, *, bwd=False,
+                ptr=1 << 12, ws=None, ws_bytes=0):
+    """attn_fwd_ex / attn_bwd_ex with placeholder addresses, for variants
+    that must fail host validation (nothing may launch); returns (status,
+    message)."""
+    L = lib()
+    sp = ctypes.byref(segments) if segments else None
+    if bwd:
+        st = L.attn_bwd_ex(ctypes.byref(desc), sp, ctypes.byref(var), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                           ws, ws_bytes, None, None)
+    else:
+        st = L.attn_fwd_ex(ctypes.byref(desc), sp, ctypes.byref(var), ptr, ptr, ptr, ptr, ptr, ws, ws_bytes, None,
+                           None)
+    return st, L.attn_last_error().decode(errors="replace")
+
+
+def ex_workspace_sizes(desc: attn_desc, var: attn_variant | None, segments: attn_segments | None = None):
+    L = lib()
+    sp = ctypes.byref(segments) if segments else None
+    vp = ctypes.byref(var) if var is not None else None
+    return (L.attn_fwd_ex_workspace_size(ctypes.byref(desc), sp, vp),
+            L.attn_bwd_ex_workspace_size(ctypes.byref(desc), sp, vp))

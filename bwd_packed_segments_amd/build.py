@@ -56,11 +56,14 @@ def units():
     out.append(("seg_meta", [os.path.join(CSRC, "seg_meta.hip")], []))
     out.append(("ring", [os.path.join(CSRC, "ring.hip")], []))
     out.append(("attn_api", ["-x", "hip", os.path.join(CSRC, "attn_api.cpp")], []))
+    out.append(("variant", [os.path.join(CSRC, "variant.hip")], []))
     for t, dqk, dv in INSTANCES:
         for part, tag in ((0, "fwd"), (1, "dq"), (2, "dkdv")):
-            name = f"attn_{tag}_{t}_{dqk}_{dv}"
-            out.append((name, [os.path.join(CSRC, "attn_inst.hip")],
-                        [f"-DINST_T={t}", f"-DINST_DQK={dqk}", f"-DINST_DV={dv}", f"-DINST_PART={part}"]))
+            for var in (0, 1):
+                name = f"attn_{tag}_{t}_{dqk}_{dv}" + ("_var" if var else "")
+                out.append((name, [os.path.join(CSRC, "attn_inst.hip")],
+                            [f"-DINST_T={t}", f"-DINST_DQK={dqk}", f"-DINST_DV={dv}", f"-DINST_PART={part}",
+                             f"-DINST_VAR={var}"]))
     return out
 
 

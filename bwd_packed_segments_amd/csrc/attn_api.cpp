@@ -201,20 +201,30 @@ attn_status prepare_segments(const attn_desc* d, const attn_segments* seg, const
 #define BPS_BF16_DIMS(X) X(64, 64) X(64, 128) X(128, 64) X(128, 128) X(192, 64) X(192, 128)
 #define BPS_FP32_DIMS(X) X(64, 64) X(64, 128) X(128, 64) X(128, 128)
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t run_bwd_phases(int phases, const bps::BwdArgs& a, hipStream_t st) {
   hipError_t e = hipSuccess;
-  if ((phases & ATTN_BWD_PREPARE) && (e = bps::launch_bwd_delta<T, DQK, DV>(a, st)) != hipSuccess) return e;
-  if ((phases & ATTN_BWD_DKDV) && (e = bps::launch_bwd_dkdv<T, DQK, DV>(a, st)) != hipSuccess) return e;
-  if ((phases & ATTN_BWD_DQ) && (e = bps::launch_bwd_dq<T, DQK, DV>(a, st)) != hipSuccess) return e;
+  if ((phases & ATTN_BWD_PREPARE) && (e = bps::launch_bwd_delta<T, DQK, DV, VAR>(a, st)) != hipSuccess) return e;
+  if ((phases & ATTN_BWD_DKDV) && (e = bps::launch_bwd_dkdv<T, DQK, DV, VAR>(a, st)) != hipSuccess) return e;
+  if ((phases & ATTN_BWD_DQ) && (e = bps::launch_bwd_dq<T, DQK, DV, VAR>(a, st)) != hipSuccess) return e;
   return e;
 }
 
-hipError_t dispatch_fwd(int dtype, int dqk, int dv, const bps::FwdArgs& a, hipStream_t st) {
+template <typename T, int DQK, int DV>
+hipError_t run_fwd(bool var, const bps::FwdArgs& a, hipStream_t st) {
+  return var ? bps::launch_fwd<T, DQK, DV, true>(a, st) : bps::launch_fwd<T, DQK, DV, false>(a, st);
+}
+
+template <typename T, int DQK, int DV>
+hipError_t run_bwd(int phases, bool var, const bps::BwdArgs& a, hipStream_t st) {
+  return var ? run_bwd_phases<T, DQK, DV, true>(phases, a, st) : run_bwd_phases<T, DQK, DV, false>(phases, a, st);
+}
+
+hipError_t dispatch_fwd(int dtype, int dqk, int dv, bool var, const bps::FwdArgs& a, hipStream_t st) {
 #define BPS_FWD_BF16(DQK, DV) \
-  if (dqk == DQK && dv == DV) return bps::launch_fwd<bps::bf16, DQK, DV>(a, st);
+  if (dqk == DQK && dv == DV) return run_fwd<bps::bf16, DQK, DV>(var, a, st);
 #define BPS_FWD_FP32(DQK, DV) \
-  if (dqk == DQK && dv == DV) return bps::launch_fwd<float, DQK, DV>(a, st);
+  if (dqk == DQK && dv == DV) return run_fwd<float, DQK, DV>(var, a, st);
   if (dtype == ATTN_BF16) {
     BPS_BF16_DIMS(BPS_FWD_BF16)
   } else {
@@ -225,11 +235,11 @@ hipError_t dispatch_fwd(int dtype, int dqk, int dv, const bps::FwdArgs& a, hipSt
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_bwd(int phases, int dtype, int dqk, int dv, const bps::BwdArgs& a, hipStream_t st) {
+hipError_t dispatch_bwd(int phases, int dtype, int dqk, int dv, bool var, const bps::BwdArgs& a, hipStream_t st) {
 #define BPS_BWD_BF16(DQK, DV) \
-  if (dqk == DQK && dv == DV) return run_bwd_phases<bps::bf16, DQK, DV>(phases, a, st);
+  if (dqk == DQK && dv == DV) return run_bwd<bps::bf16, DQK, DV>(phases, var, a, st);
 #define BPS_BWD_FP32(DQK, DV) \
-  if (dqk == DQK && dv == DV) return run_bwd_phases<float, DQK, DV>(phases, a, st);
+  if (dqk == DQK && dv == DV) return run_bwd<float, DQK, DV>(phases, var, a, st);
   if (dtype == ATTN_BF16) {
     BPS_BF16_DIMS(BPS_BWD_BF16)
   } else {
@@ -374,6 +384,196 @@ const char* cadd(const void* base, size_t elems, size_t esize) {
 }
 char* madd(void* base, size_t elems, size_t esize) { return static_cast<char*>(base) + elems * esize; }
 
+
+// ------------------------------------------------------------ variants
+
+// Workspace and checks of the variant arguments (attn_variant).  The plain
+// workspace layout of make_plan is a prefix of the variant one.
+struct VarPlan {
+  bool on = false;            // any variant requested: the VAR kernels run
+  bool dbias_partial = false; // one bias slab for several batch rows: fp32 partials, then a sum
+  size_t n_ml = 0;            // max-logit partials per head
+  size_t off_ml = 0, off_dsink = 0, off_dbias = 0;
+  size_t ws_fwd = 0, ws_bwd = 0;
+};
+
+attn_status make_var_plan(const attn_desc* d, const Plan& p, const attn_variant* var, VarPlan* vp) {
+  vp->ws_fwd = p.ws_fwd;
+  vp->ws_bwd = p.ws_bwd;
+  if (!var) return ATTN_OK;
+  if (!std::isfinite(var->softcap) || var->softcap < 0.f)
+    return fail(ATTN_E_INVALID, "softcap must be finite and >= 0");
+  if (var->bias && var->bias_batch != 1 && var->bias_batch != d->B)
+    return fail(ATTN_E_INVALID, "bias_batch must be 1 or B (%d), got %d", d->B, var->bias_batch);
+  if (var->dbias && !var->bias) return fail(ATTN_E_INVALID, "dbias requested without a bias");
+  if (var->dsink && !var->sink) return fail(ATTN_E_INVALID, "dsink requested without sink logits");
+  if ((var->bias && reinterpret_cast<uintptr_t>(var->bias) % 16) ||
+      (var->dbias && reinterpret_cast<uintptr_t>(var->dbias) % 16))
+    return fail(ATTN_E_UNSUPPORTED, "bias and dbias must be 16-byte aligned");
+  if ((var->sink && reinterpret_cast<uintptr_t>(var->sink) % 4) ||
+      (var->max_logit && reinterpret_cast<uintptr_t>(var->max_logit) % 4) ||
+      (var->dsink && reinterpret_cast<uintptr_t>(var->dsink) % 4))
+    return fail(ATTN_E_INVALID, "sink, max_logit and dsink must be 4-byte aligned");
+  vp->on = var->bias || var->softcap > 0.f || var->sink || var->max_logit || var->dbias || var->dsink;
+  if (!vp->on) return ATTN_OK;
+  size_t off = p.ws_fwd;
+  if (var->max_logit) {
+    const size_t n_qt = (d->Sq + 127) / 128;   // forward query tiles of 128 rows, 4 waves each
+    vp->n_ml = (size_t)d->B * n_qt * 4;
+    vp->off_ml = off;
+    off = align_up(off + vp->n_ml * d->Hq * sizeof(float));
+  }
+  vp->ws_fwd = off;
+  off = p.ws_bwd;
+  const size_t nrow = (size_t)d->B * d->Hq * d->Sq;
+  if (var->dsink) {
+    vp->off_dsink = off;
+    off = align_up(off + nrow * sizeof(float));
+  }
+  vp->dbias_partial = var->dbias && var->bias_batch == 1 && d->B > 1;
+  if (vp->dbias_partial) {
+    vp->off_dbias = off;
+    off = align_up(off + nrow * (size_t)d->Skv * sizeof(float));
+  }
+  vp->ws_bwd = off;
+  return ATTN_OK;
+}
+
+bps::VarView var_view(const attn_desc* d, const attn_variant* var, const VarPlan& vp, char* ws, bool bwd) {
+  bps::VarView v{};
+  if (!vp.on) return v;
+  const int64_t slab = (int64_t)d->Hq * d->Sq * d->Skv;
+  v.bias = var->bias;
+  v.bias_b = (var->bias && var->bias_batch > 1) ? slab : 0;
+  v.softcap = var->softcap;
+  v.cap_k = var->softcap > 0.f ? 2.f * bps::kLog2e / var->softcap : 0.f;
+  v.cap_l2 = var->softcap * bps::kLog2e;
+  v.cap_inv = var->softcap > 0.f ? 1.f / v.cap_l2 : 0.f;
+  v.sink = var->sink;
+  if (!bwd) {
+    v.ml_part = var->max_logit ? reinterpret_cast<float*>(ws + vp.off_ml) : nullptr;
+    return v;
+  }
+  if (var->dbias) {
+    v.dbias = vp.dbias_partial ? static_cast<void*>(ws + vp.off_dbias) : var->dbias;
+    v.dbias_f32 = vp.dbias_partial ? 1 : 0;
+    v.dbias_b = (vp.dbias_partial || var->bias_batch > 1) ? slab : 0;
+  }
+  v.dsink_row = var->dsink ? reinterpret_cast<float*>(ws + vp.off_dsink) : nullptr;
+  return v;
+}
+
+attn_status fwd_impl(const attn_desc* d, const attn_segments* seg, const attn_variant* var, const void* q,
+                     const void* k, const void* v, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream, int32_t* route_out) {
+  try {
+    Plan p;
+    attn_status st = make_plan(d, seg, &p);
+    if (st != ATTN_OK) return st;
+    VarPlan vp;
+    if ((st = make_var_plan(d, p, var, &vp)) != ATTN_OK) return st;
+    const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
+    if (need_nonnull(q, nq) || need_nonnull(o, nq) || need_nonnull(lse, nq))
+      return fail(ATTN_E_INVALID, "q, o and lse must not be NULL");
+    if (need_nonnull(k, nkv) || need_nonnull(v, nkv)) return fail(ATTN_E_INVALID, "k and v must not be NULL");
+    if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
+        (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)))
+      return st;
+    if ((st = check_ws(workspace, workspace_bytes, vp.ws_fwd)) != ATTN_OK) return st;
+    if (route_out) *route_out = route_of(p);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    bps::FwdArgs a{};
+    a.s = shape_of(d, p);
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
+    a.var = var_view(d, var, vp, ws, false);
+    if (d->Sq > 0) {
+      if ((st = prepare_segments(d, seg, p, ws, hs, &a.seg)) != ATTN_OK) return st;
+      hipError_t e = dispatch_fwd(d->dtype, d->Dqk, d->Dv, vp.on, a, hs);
+      if (e != hipSuccess) return fail(ATTN_E_DEVICE, "forward launch: %s", hipGetErrorString(e));
+    }
+    if (vp.on && var->max_logit) {
+      hipError_t e = bps::launch_max_logit_reduce(a.var.ml_part, vp.n_ml, d->Hq, var->max_logit, hs);
+      if (e != hipSuccess) return fail(ATTN_E_DEVICE, "max-logit launch: %s", hipGetErrorString(e));
+    }
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
+}
+
+attn_status bwd_impl(int32_t phases, const attn_desc* d, const attn_segments* seg, const attn_variant* var,
+                     const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream,
+                     int32_t* route_out) {
+  try {
+    if (phases <= 0 || (phases & ~ATTN_BWD_ALL))
+      return fail(ATTN_E_INVALID, "phases must be a nonzero combination of ATTN_BWD_* bits (got %d)", phases);
+    Plan p;
+    attn_status st = make_plan(d, seg, &p);
+    if (st != ATTN_OK) return st;
+    VarPlan vp;
+    if ((st = make_var_plan(d, p, var, &vp)) != ATTN_OK) return st;
+    const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
+    if (need_nonnull(dout, nq)) return fail(ATTN_E_INVALID, "dout must not be NULL");
+    if ((phases & ATTN_BWD_PREPARE) && (need_nonnull(o, nq) || need_nonnull(lse, nq)))
+      return fail(ATTN_E_INVALID, "o and lse must not be NULL");
+    if ((phases & (ATTN_BWD_DKDV | ATTN_BWD_DQ)) && (need_nonnull(q, nq) || need_nonnull(k, nkv) || need_nonnull(v, nkv)))
+      return fail(ATTN_E_INVALID, "q, k and v must not be NULL");
+    if ((phases & ATTN_BWD_DQ) && need_nonnull(dq, nq)) return fail(ATTN_E_INVALID, "dq must not be NULL");
+    if ((phases & ATTN_BWD_DKDV) && (need_nonnull(dk, nkv) || need_nonnull(dv, nkv)))
+      return fail(ATTN_E_INVALID, "dk and dv must not be NULL");
+    if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
+        (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)) ||
+        (st = check_align("dout", dout, d->dtype)) || (st = check_align("dq", dq, d->dtype)) ||
+        (st = check_align("dk", dk, d->dtype)) || (st = check_align("dv", dv, d->dtype)))
+      return st;
+    if ((st = check_ws(workspace, workspace_bytes, vp.ws_bwd)) != ATTN_OK) return st;
+    if (route_out) *route_out = route_of(p);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    bps::BwdArgs a{};
+    a.s = shape_of(d, p);
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
+    a.delta = reinterpret_cast<float*>(ws + p.off_delta);
+    a.lse2 = reinterpret_cast<float*>(ws + p.off_lse2);
+    a.var = var_view(d, var, vp, ws, true);
+    const bool prep = (phases & ATTN_BWD_PREPARE) != 0;
+    const size_t esize = d->dtype == ATTN_BF16 ? 2 : 4;
+    const size_t slab = (size_t)d->Hq * d->Sq * d->Skv;
+    hipError_t e = hipSuccess;
+    // Variants, before the attention kernels: the dbias target starts at zero
+    // (dK/dV writes only the tiles it visits).
+    if (prep && vp.on && var->dbias) {
+      e = vp.dbias_partial ? bps::launch_zero_fill(a.var.dbias, (size_t)d->B * slab * sizeof(float), hs)
+                           : bps::launch_zero_fill(var->dbias, (size_t)var->bias_batch * slab * esize, hs);
+      if (e != hipSuccess) return fail(ATTN_E_DEVICE, "dbias fill launch: %s", hipGetErrorString(e));
+    }
+    if (!(d->Sq == 0 && d->Skv == 0)) {
+      if ((st = prepare_segments(d, seg, p, ws, hs, &a.seg, prep)) != ATTN_OK) return st;
+      e = dispatch_bwd(phases, d->dtype, d->Dqk, d->Dv, vp.on, a, hs);
+      if (e != hipSuccess) return fail(ATTN_E_DEVICE, "backward launch: %s", hipGetErrorString(e));
+    }
+    // Variants, after: the per-head sink gradient (from the prepare phase's
+    // per-row terms) and the sum of the dbias partials over batch rows.
+    if (prep && vp.on && var->dsink) {
+      e = bps::launch_dsink_reduce(a.var.dsink_row, d->B, d->Hq, d->Sq, var->dsink, hs);
+      if (e != hipSuccess) return fail(ATTN_E_DEVICE, "dsink launch: %s", hipGetErrorString(e));
+    }
+    if ((phases & ATTN_BWD_DKDV) && vp.dbias_partial) {
+      e = bps::launch_dbias_reduce(d->dtype == ATTN_BF16, static_cast<const float*>(a.var.dbias), d->B, slab,
+                                   var->dbias, hs);
+      if (e != hipSuccess) return fail(ATTN_E_DEVICE, "dbias sum launch: %s", hipGetErrorString(e));
+    }
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,77 +591,15 @@ size_t attn_bwd_workspace_size(const attn_desc* desc, const attn_segments* seg) 
 attn_status attn_fwd(const attn_desc* d, const attn_segments* seg, const void* q, const void* k, const void* v,
                      void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream,
                      int32_t* route_out) {
-  try {
-    Plan p;
-    attn_status st = make_plan(d, seg, &p);
-    if (st != ATTN_OK) return st;
-    const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
-    if (need_nonnull(q, nq) || need_nonnull(o, nq) || need_nonnull(lse, nq))
-      return fail(ATTN_E_INVALID, "q, o and lse must not be NULL");
-    if (need_nonnull(k, nkv) || need_nonnull(v, nkv)) return fail(ATTN_E_INVALID, "k and v must not be NULL");
-    if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
-        (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)))
-      return st;
-    if ((st = check_ws(workspace, workspace_bytes, p.ws_fwd)) != ATTN_OK) return st;
-    if (route_out) *route_out = route_of(p);
-    if (d->Sq == 0) return ATTN_OK;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    bps::FwdArgs a{};
-    a.s = shape_of(d, p);
-    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
-    if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg)) != ATTN_OK) return st;
-    hipError_t e = dispatch_fwd(d->dtype, d->Dqk, d->Dv, a, hs);
-    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "forward launch: %s", hipGetErrorString(e));
-    return ATTN_OK;
-  } catch (...) {
-    return fail(ATTN_E_DEVICE, "unexpected host exception");
-  }
+  return fwd_impl(d, seg, nullptr, q, k, v, o, lse, workspace, workspace_bytes, stream, route_out);
 }
 
 attn_status attn_bwd_phase(int32_t phases, const attn_desc* d, const attn_segments* seg, const void* q,
                            const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
                            void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream,
                            int32_t* route_out) {
-  try {
-    if (phases <= 0 || (phases & ~ATTN_BWD_ALL))
-      return fail(ATTN_E_INVALID, "phases must be a nonzero combination of ATTN_BWD_* bits (got %d)", phases);
-    Plan p;
-    attn_status st = make_plan(d, seg, &p);
-    if (st != ATTN_OK) return st;
-    const long long nq = (long long)d->B * d->Sq * d->Hq, nkv = (long long)d->B * d->Skv * d->Hkv;
-    if (need_nonnull(dout, nq)) return fail(ATTN_E_INVALID, "dout must not be NULL");
-    if ((phases & ATTN_BWD_PREPARE) && (need_nonnull(o, nq) || need_nonnull(lse, nq)))
-      return fail(ATTN_E_INVALID, "o and lse must not be NULL");
-    if ((phases & (ATTN_BWD_DKDV | ATTN_BWD_DQ)) && (need_nonnull(q, nq) || need_nonnull(k, nkv) || need_nonnull(v, nkv)))
-      return fail(ATTN_E_INVALID, "q, k and v must not be NULL");
-    if ((phases & ATTN_BWD_DQ) && need_nonnull(dq, nq)) return fail(ATTN_E_INVALID, "dq must not be NULL");
-    if ((phases & ATTN_BWD_DKDV) && (need_nonnull(dk, nkv) || need_nonnull(dv, nkv)))
-      return fail(ATTN_E_INVALID, "dk and dv must not be NULL");
-    if ((st = check_align("q", q, d->dtype)) || (st = check_align("k", k, d->dtype)) ||
-        (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)) ||
-        (st = check_align("dout", dout, d->dtype)) || (st = check_align("dq", dq, d->dtype)) ||
-        (st = check_align("dk", dk, d->dtype)) || (st = check_align("dv", dv, d->dtype)))
-      return st;
-    if ((st = check_ws(workspace, workspace_bytes, p.ws_bwd)) != ATTN_OK) return st;
-    if (route_out) *route_out = route_of(p);
-    if (d->Sq == 0 && d->Skv == 0) return ATTN_OK;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    bps::BwdArgs a{};
-    a.s = shape_of(d, p);
-    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
-    a.dq = dq; a.dk = dk; a.dv = dv;
-    a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
-    a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_delta);
-    a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_lse2);
-    const bool prep = (phases & ATTN_BWD_PREPARE) != 0;
-    if ((st = prepare_segments(d, seg, p, static_cast<char*>(workspace), hs, &a.seg, prep)) != ATTN_OK) return st;
-    hipError_t e = dispatch_bwd(phases, d->dtype, d->Dqk, d->Dv, a, hs);
-    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "backward launch: %s", hipGetErrorString(e));
-    return ATTN_OK;
-  } catch (...) {
-    return fail(ATTN_E_DEVICE, "unexpected host exception");
-  }
+  return bwd_impl(phases, d, seg, nullptr, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream,
+                  route_out);
 }
 
 attn_status attn_bwd(const attn_desc* d, const attn_segments* seg, const void* q, const void* k, const void* v,
@@ -469,6 +607,42 @@ attn_status attn_bwd(const attn_desc* d, const attn_segments* seg, const void* q
                      void* workspace, size_t workspace_bytes, void* stream, int32_t* route_out) {
   return attn_bwd_phase(ATTN_BWD_ALL, d, seg, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
                         stream, route_out);
+}
+
+size_t attn_fwd_ex_workspace_size(const attn_desc* desc, const attn_segments* seg, const attn_variant* var) {
+  Plan p;
+  VarPlan vp;
+  if (make_plan(desc, seg, &p) != ATTN_OK || make_var_plan(desc, p, var, &vp) != ATTN_OK) return 0;
+  return vp.ws_fwd;
+}
+
+size_t attn_bwd_ex_workspace_size(const attn_desc* desc, const attn_segments* seg, const attn_variant* var) {
+  Plan p;
+  VarPlan vp;
+  if (make_plan(desc, seg, &p) != ATTN_OK || make_var_plan(desc, p, var, &vp) != ATTN_OK) return 0;
+  return vp.ws_bwd;
+}
+
+attn_status attn_fwd_ex(const attn_desc* d, const attn_segments* seg, const attn_variant* var, const void* q,
+                        const void* k, const void* v, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream, int32_t* route_out) {
+  return fwd_impl(d, seg, var, q, k, v, o, lse, workspace, workspace_bytes, stream, route_out);
+}
+
+attn_status attn_bwd_ex_phase(int32_t phases, const attn_desc* d, const attn_segments* seg, const attn_variant* var,
+                              const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, void* stream, int32_t* route_out) {
+  return bwd_impl(phases, d, seg, var, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream,
+                  route_out);
+}
+
+attn_status attn_bwd_ex(const attn_desc* d, const attn_segments* seg, const attn_variant* var, const void* q,
+                        const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                        void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream,
+                        int32_t* route_out) {
+  return bwd_impl(ATTN_BWD_ALL, d, seg, var, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream,
+                  route_out);
 }
 
 attn_status attn_debug_mask(const attn_desc* d, const attn_segments* seg, uint8_t* mask_out, int32_t* route_rows,

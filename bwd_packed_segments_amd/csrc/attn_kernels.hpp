@@ -116,6 +116,81 @@ __device__ inline void stage_kv_meta(const SegView& sv, int b, int Skv, int k0, 
   }
 }
 
+// ------------------------------------------------------------ variants
+
+// Base-2 logit of one pair under the variants: x = raw * scale + bias
+// (natural units), soft-capped to softcap * tanh(x / softcap) when a cap is
+// set, times log2(e).  tanh(y) = 1 - 2 / (exp(2y) + 1), which saturates to
+// +-1 as |y| grows, so a capped logit is always finite.
+__device__ inline float var_logit2(float raw, float bias, float scale, const VarView& v) {
+  const float x = fmaf(raw, scale, bias);
+  if (v.softcap > 0.f) {
+    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(x * v.cap_k) + 1.f);
+    return t * v.cap_l2;
+  }
+  return x * kLog2e;
+}
+
+// dS/dx at a base-2 logit s2: 1 - tanh^2 under soft-capping (tanh = s2 /
+// (softcap log2 e); a masked logit, -inf, gives 0), 1 otherwise.
+__device__ inline float var_dx_factor(float s2, const VarView& v) {
+  if (v.softcap > 0.f) {
+    const float t = s2 * v.cap_inv;
+    return fmaxf(1.f - t * t, 0.f);
+  }
+  return 1.f;
+}
+
+// Variant logits of a 32x32 tile with keys in rows (S^T in the forward and
+// dQ kernels): brow is the bias row of the lane's query (NULL: no bias, or
+// a query past Sq), the keys are kbase + rmap(hf, r).
+template <typename T>
+__device__ inline void var_tile_keys(f32x16& x, const VarView& v, const T* brow, int kbase, int Skv, float scale,
+                                     int hf) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = kbase + rmap(hf, r);
+    const float bv = (brow != nullptr && j < Skv) ? (float)brow[j] : 0.f;
+    x[r] = var_logit2(x[r], bv, scale, v);
+  }
+}
+
+// The same with queries in rows (S in the dK/dV kernels): bcol is the bias
+// column of the lane's key (queries Skv elements apart; NULL: no bias, or a
+// key past Skv), the queries are ibase + rmap(hf, r).
+template <typename T>
+__device__ inline void var_tile_queries(f32x16& x, const VarView& v, const T* bcol, int ibase, int Sq, int Skv,
+                                        float scale, int hf) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = ibase + rmap(hf, r);
+    const float bv = (bcol != nullptr && i < Sq) ? (float)bcol[(size_t)i * Skv] : 0.f;
+    x[r] = var_logit2(x[r], bv, scale, v);
+  }
+}
+
+// dLoss/dx of a dK/dV tile (queries in rows, the lane's key fixed) into the
+// dbias target; col is the element offset of (batch row, head, query 0, key).
+template <typename T>
+__device__ inline void var_store_dx(const f32x16& dx, const VarView& v, size_t col, int ibase, int Sq, int Skv,
+                                    int hf) {
+  if (v.dbias_f32) {
+    float* p = static_cast<float*>(v.dbias) + col;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = ibase + rmap(hf, r);
+      if (i < Sq) p[(size_t)i * Skv] = dx[r];
+    }
+  } else {
+    T* p = static_cast<T*>(v.dbias) + col;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = ibase + rmap(hf, r);
+      if (i < Sq) p[(size_t)i * Skv] = static_cast<T>(dx[r]);
+    }
+  }
+}
+
 // ------------------------------------------------------------ forward
 
 template <typename T, int DQK, int DV>
@@ -130,7 +205,7 @@ struct FwdCfg {
   static constexpr int WAVES_PER_EU = Staging<T, STAGE_BYTES>::WAVES_PER_EU;
 };
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, DQK, DV>::WAVES_PER_EU)))
     attn_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<T, DQK, DV>;
@@ -221,9 +296,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
     if (general) stage_kv_meta<BN>(a.seg, b, s.Skv, k0, kid, tid, nvalid == BN);
   };
 
-  const float c2 = s.scale_log2;
-  float m = -INFINITY;   // reference max of the raw scores (rescaled lazily)
+  // Without variants the scores stay raw (c2 folds in the scale); with
+  // them they are turned into base-2 logits first (c2 = 1).
+  const float c2 = VAR ? 1.f : s.scale_log2;
+  float m = -INFINITY;   // reference max of the scores (rescaled lazily)
   float l = 0.f;         // this lane half's partial sum of exp2((s - m) * c2)
+  float mxe = -INFINITY; // exact max of this query's allowed logits (base 2)
+  const T* brow = nullptr;
+  if constexpr (VAR) {
+    if (a.var.bias != nullptr && qi < s.Sq)
+      brow = static_cast<const T*>(a.var.bias) + b * a.var.bias_b + ((size_t)h * s.Sq + qi) * s.Skv;
+  }
   f32x16 o[DV / 32];
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
@@ -252,6 +335,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
         sacc[blk] = mma(frag_row<T, DQK>(Ks, blk * 32 + n, 16 * t + 8 * hf), qf[t], sacc[blk]);
+    if constexpr (VAR) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) var_tile_keys<T>(sacc[blk], a.var, brow, k0 + blk * 32, s.Skv, s.scale, hf);
+    }
 
     if (cls == kTilePart) {
 #pragma unroll
@@ -268,6 +355,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[blk][r]);
     mx = wave_xor32_max(mx);
+    if constexpr (VAR) mxe = fmaxf(mxe, mx);
     const bool grow = mx > m && (m == -INFINITY || (mx - m) * c2 > 8.f);
     if (__any(grow)) {
       const float m_new = grow ? mx : m;
@@ -314,7 +402,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
   // Epilogue: O = O^T / l, LSE = m * scale + ln(l); empty rows give O = 0,
   // LSE = -inf.
   const float lt = wave_xor32_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float lse = lt > 0.f ? m * s.scale + logf(lt) : -INFINITY;
+  if constexpr (VAR) {
+    // m is a base-2 logit here.  The sink adds exp2(sink2 - m) to the sum
+    // of terms; the reference moves to the larger of the two so that no
+    // term overflows.  A row with no allowed key then has O = 0 and
+    // LSE = sink.
+    float ref = m, tot = lt, alpha = 1.f;
+    if (a.var.sink != nullptr) {
+      const float s2 = a.var.sink[h] * kLog2e;
+      if (lt > 0.f) {
+        ref = fmaxf(m, s2);
+        alpha = fast_exp2(m - ref);
+        tot = lt * alpha + fast_exp2(s2 - ref);
+      } else {
+        ref = s2;
+        alpha = 0.f;
+        tot = 1.f;
+      }
+    }
+    inv = tot > 0.f ? alpha / tot : 0.f;
+    lse = tot > 0.f ? ref * kLn2 + logf(tot) : -INFINITY;
+    if (a.var.ml_part != nullptr) {
+      float wm = qi < s.Sq ? mxe : -INFINITY;
+#pragma unroll
+      for (int d = 1; d < 32; d <<= 1) wm = fmaxf(wm, __shfl_xor(wm, d));
+      if (lane == 0) a.var.ml_part[(((size_t)h * s.B + b) * n_qt + qt) * 4 + wave] = wm * kLn2;
+    }
+  }
   if (qi < s.Sq) {
     T* op = static_cast<T*>(a.o) + b * a.so.b + qi * a.so.t + h * a.so.h;
 #pragma unroll
@@ -324,14 +440,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
         f32x4 x = f32x4{o[d][4 * grp], o[d][4 * grp + 1], o[d][4 * grp + 2], o[d][4 * grp + 3]} * inv;
         *reinterpret_cast<typename E::P4*>(op + d * 32 + 8 * grp + 4 * hf) = E::cvt4(x);
       }
-    if (hf == 0)
-      a.lse[((size_t)b * s.Hq + h) * s.Sq + qi] = lt > 0.f ? m * s.scale + logf(lt) : -INFINITY;
+    if (hf == 0) a.lse[((size_t)b * s.Hq + h) * s.Sq + qi] = lse;
   }
 }
 
 // ------------------------------------------------------------ backward: Delta
 
-template <typename T, int DV>
+template <typename T, int DV, bool VAR>
 __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F8 = typename E::F8;
@@ -364,7 +479,13 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(BwdArgs a) {
     const size_t x = ((size_t)b * s.Hq + h) * s.Sq + i;
     a.delta[x] = acc;
     const float lse = a.lse[x];
-    a.lse2[x] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    a.lse2[x] = lse2;
+    // The sink's share of the row, exp(sink - LSE), times -Delta: this
+    // row's term of dLoss/dsink.
+    if constexpr (VAR) {
+      if (a.var.dsink_row != nullptr) a.var.dsink_row[x] = -fast_exp2(a.var.sink[h] * kLog2e - lse2) * acc;
+    }
   }
 }
 
@@ -383,7 +504,7 @@ struct DqCfg {
   static constexpr int WAVES_PER_EU = (DQK > 128 || DQK + DV > 256) ? 1 : Staging<T, STAGE_BYTES>::WAVES_PER_EU;
 };
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, DQK, DV>::WAVES_PER_EU)))
     attn_bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<T, DQK, DV>;
@@ -482,6 +603,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<
   };
 
   const float c2 = s.scale_log2;
+  const T* brow = nullptr;
+  if constexpr (VAR) {
+    if (a.var.bias != nullptr && qi < s.Sq)
+      brow = static_cast<const T*>(a.var.bias) + b * a.var.bias_b + ((size_t)h * s.Sq + qi) * s.Skv;
+  }
   f32x16 dqa[DQK / 32];
 #pragma unroll
   for (int d = 0; d < DQK / 32; ++d) dqa[d] = f32x16{};
@@ -511,13 +637,26 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<
       for (int t = 0; t < DQK / 16; ++t) sacc = mma(frag_row<T, DQK>(Ks, blk * 32 + n, 16 * t + 8 * hf), qf[t], sacc);
 #pragma unroll
       for (int t = 0; t < DV / 16; ++t) pacc = mma(frag_row<T, DV>(Vs, blk * 32 + n, 16 * t + 8 * hf), dof[t], pacc);
-      // P = exp2(S * scale * log2e - LSE2); dS = P * (dP - Delta).
+      if constexpr (VAR) {
+        // Variant logits, masked to -inf, then P and dLoss/dx = P (dP -
+        // Delta) dS/dx in one pass.
+        var_tile_keys<T>(sacc, a.var, brow, k0 + blk * 32, s.Skv, s.scale, hf);
+        if (cls == kTilePart)
+          mask_tile<true>(sacc, -INFINITY, route, causal, s.Skv, qi, qm, k0 + blk * 32, hf, kid, kid + BN, blk * 32);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c2, -lse2));
-      if (cls == kTilePart)
-        mask_tile<true>(sacc, 0.f, route, causal, s.Skv, qi, qm, k0 + blk * 32, hf, kid, kid + BN, blk * 32);
+        for (int r = 0; r < 16; ++r) {
+          const float s2 = sacc[r];
+          sacc[r] = fast_exp2(s2 - lse2) * (pacc[r] - delta) * var_dx_factor(s2, a.var);
+        }
+      } else {
+        // P = exp2(S * scale * log2e - LSE2); dS = P * (dP - Delta).
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = sacc[r] * (pacc[r] - delta);
+        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c2, -lse2));
+        if (cls == kTilePart)
+          mask_tile<true>(sacc, 0.f, route, causal, s.Skv, qi, qm, k0 + blk * 32, hf, kid, kid + BN, blk * 32);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = sacc[r] * (pacc[r] - delta);
+      }
       // dQ^T += K^T dS^T, K^T read from the row-major K tile by transpose loads.
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -571,7 +710,7 @@ struct DkvCfg {
   static constexpr int WAVES_PER_EU = 1;
 };
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg<T, DQK, DV>::WAVES_PER_EU)))
     attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = DkvCfg<T, DQK, DV>;
@@ -721,6 +860,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
     const int* qmb = qma + BM;
     const int i0 = tile_of(x) * BM;
     constexpr int NQB = BM / 32;
+    const T* bcol = nullptr;   // variants: bias column of this lane's key
+    size_t dcol = 0;           // and its offset in the dbias target
+    if constexpr (VAR) {
+      const size_t col = (size_t)(hkv * g + x % g) * s.Sq * s.Skv + kj;
+      if (a.var.bias != nullptr && kj < s.Skv) bcol = static_cast<const T*>(a.var.bias) + b * a.var.bias_b + col;
+      dcol = b * a.var.dbias_b + col;
+    }
 
     auto sdp = [&](int qb, f32x16& sa, f32x16& pa) {
       F8 qa[DQK / 16], da[DV / 16];
@@ -738,18 +884,38 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
     // P = exp2(S * scale * log2e - LSE2), dS = P * (dP - Delta); returns the
     // bf16 operands of the dV and dK products.
     auto softgrad = [&](int qb, f32x16& sa, f32x16& pa, F8* pf, F8* dsf) {
+      if constexpr (VAR) {
+        // Variant logits, masked to -inf, then P and dLoss/dx = P (dP -
+        // Delta) dS/dx in one pass; dx also goes to the dbias target.
+        var_tile_queries<T>(sa, a.var, bcol, i0 + qb * 32, s.Sq, s.Skv, s.scale, hf);
+        if (part) mask_tile<false>(sa, -INFINITY, route, causal, s.Skv, kj, km, i0 + qb * 32, hf, qma, qmb, qb * 32);
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
+        for (int grp = 0; grp < 4; ++grp) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[i]));
-      }
-      if (part) mask_tile<false>(sa, 0.f, route, causal, s.Skv, kj, km, i0 + qb * 32, hf, qma, qmb, qb * 32);
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * grp + i;
+            const float s2 = sa[r];
+            sa[r] = fast_exp2(s2 - l4[i]);
+            pa[r] = sa[r] * (pa[r] - d4[i]) * var_dx_factor(s2, a.var);
+          }
+        }
+        if (a.var.dbias != nullptr && kj < s.Skv) var_store_dx<T>(pa, a.var, dcol, i0 + qb * 32, s.Sq, s.Skv, hf);
+      } else {
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
+        for (int grp = 0; grp < 4; ++grp) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pa[4 * grp + i] = sa[4 * grp + i] * (pa[4 * grp + i] - d4[i]);
+          for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[i]));
+        }
+        if (part) mask_tile<false>(sa, 0.f, route, causal, s.Skv, kj, km, i0 + qb * 32, hf, qma, qmb, qb * 32);
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pa[4 * grp + i] = sa[4 * grp + i] * (pa[4 * grp + i] - d4[i]);
+        }
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -882,7 +1048,7 @@ struct DkvWsCfg {
   static constexpr bool ENABLED = sizeof(T) == 2 && DQK <= 192 && DV <= 128 && LDS_BYTES <= 160 * 1024;
 };
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     attn_bwd_dkdv_ws_kernel(BwdArgs a) {
   using C = DkvWsCfg<T, DQK, DV>;
@@ -1033,18 +1199,42 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     for (int t = 0; t < DQK / 16; ++t) sa = mma(qa[t], kf[t], sa);
 #pragma unroll
     for (int t = 0; t < DV / 16; ++t) pa = mma(da[t], vf[t], pa);
+    if constexpr (VAR) {
+      // Variant logits, masked to -inf, then P and dLoss/dx = P (dP - Delta)
+      // dS/dx in one pass; dx also goes to the dbias target.
+      const int ib = tile_of(x) * BM + qb * 32;
+      const size_t col = (size_t)(hkv * g + x % g) * s.Sq * s.Skv + kj;
+      const T* bcol = (a.var.bias != nullptr && kj < s.Skv)
+                          ? static_cast<const T*>(a.var.bias) + b * a.var.bias_b + col : nullptr;
+      var_tile_queries<T>(sa, a.var, bcol, ib, s.Sq, s.Skv, s.scale, hf);
+      if (part) mask_tile<false>(sa, -INFINITY, route, causal, s.Skv, kj, km, ib, hf, qma, qmb, qb * 32);
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
+      for (int grp = 0; grp < 4; ++grp) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[i]));
-    }
-    if (part) mask_tile<false>(sa, 0.f, route, causal, s.Skv, kj, km, tile_of(x) * BM + qb * 32, hf, qma, qmb, qb * 32);
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * grp + i;
+          const float s2 = sa[r];
+          sa[r] = fast_exp2(s2 - l4[i]);
+          pa[r] = sa[r] * (pa[r] - d4[i]) * var_dx_factor(s2, a.var);
+        }
+      }
+      if (a.var.dbias != nullptr && kj < s.Skv) var_store_dx<T>(pa, a.var, b * a.var.dbias_b + col, ib, s.Sq, s.Skv, hf);
+    } else {
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
+      for (int grp = 0; grp < 4; ++grp) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pa[4 * grp + i] = sa[4 * grp + i] * (pa[4 * grp + i] - d4[i]);
+        for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[i]));
+      }
+      if (part) mask_tile<false>(sa, 0.f, route, causal, s.Skv, kj, km, tile_of(x) * BM + qb * 32, hf, qma, qmb, qb * 32);
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pa[4 * grp + i] = sa[4 * grp + i] * (pa[4 * grp + i] - d4[i]);
+      }
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -1170,45 +1360,45 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 
 // ------------------------------------------------------------ launchers
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<T, DQK, DV>;
   const int n_qt = (a.s.Sq + C::BM - 1) / C::BM;
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(C::THREADS), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st) {
   const size_t rows = (size_t)a.s.B * a.s.Sq * a.s.Hq;
   if (rows == 0) return hipSuccess;
   const size_t blocks = (rows * 8 + 255) / 256;
-  hipLaunchKernelGGL((attn_bwd_delta_kernel<T, DV>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_bwd_delta_kernel<T, DV, VAR>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
   const int n_kt = (a.s.Skv + DkvCfg<T, DQK, DV>::BN - 1) / DkvCfg<T, DQK, DV>::BN;
   const long long nblocks = (long long)a.s.B * a.s.Hkv * n_kt;
   if (nblocks <= 0) return hipSuccess;
   if constexpr (DkvWsCfg<T, DQK, DV>::ENABLED) {
     static_assert(DkvWsCfg<T, DQK, DV>::BN == DkvCfg<T, DQK, DV>::BN, "same key tiling");
-    hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(512), 0, st, a);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   const int n_qt = (a.s.Sq + DqCfg<T, DQK, DV>::BM - 1) / DqCfg<T, DQK, DV>::BM;
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -22,6 +22,25 @@ struct AttnShape {
   float scale_log2;  // scale * log2(e)
 };
 
+// Attention variants (attn_fwd_ex / attn_bwd_ex).  Logits are
+// x = scale * <q, k> + bias, soft-capped to softcap * tanh(x / softcap) when
+// softcap > 0; the sink adds exp(sink[h]) to every query's softmax
+// denominator.  Read only by the kernels instantiated with VAR = true.
+struct VarView {
+  const void* bias;      // [Bb, Hq, Sq, Skv] element type of q, contiguous; NULL: none
+  int64_t bias_b;        // batch stride of bias in elements (0: one slab for every batch row)
+  float softcap;         // 0: no soft-capping
+  float cap_k;           // 2 log2(e) / softcap: exp2 argument of tanh
+  float cap_l2;          // softcap * log2(e): tanh value -> base-2 logit
+  float cap_inv;         // 1 / cap_l2
+  const float* sink;     // [Hq] natural-log sink logits, or NULL
+  float* ml_part;        // forward: [Hq][B][query tiles][4 waves] base-e maxima, or NULL
+  void* dbias;           // backward: where dK/dV writes dLoss/dx, or NULL
+  int dbias_f32;         // dbias is an fp32 array of per-batch-row partials
+  int64_t dbias_b;       // batch stride of dbias in elements
+  float* dsink_row;      // backward: [B, Hq, Sq] -exp(sink - LSE) * Delta, or NULL
+};
+
 struct FwdArgs {
   AttnShape s;
   const void* q;
@@ -31,6 +50,7 @@ struct FwdArgs {
   float* lse;
   Strides sq, sk, sv, so;
   SegView seg;
+  VarView var;
 };
 
 struct BwdArgs {
@@ -48,6 +68,7 @@ struct BwdArgs {
   float* delta;      // [B, Hq, Sq] workspace: rowsum(dO * O)
   float* lse2;       // [B, Hq, Sq] workspace: LSE * log2(e), +inf for empty rows
   SegView seg;
+  VarView var;
 };
 
 struct SegMetaArgs {
@@ -114,13 +135,23 @@ hipError_t launch_ring_reduce(int dtype_bf16, const RingReduceArgs& a, hipStream
 hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st);
 hipError_t launch_debug_mask(const MaskArgs& a, hipStream_t st);
 
-template <typename T, int DQK, int DV>
+// VAR selects the kernels that apply the variants of VarView.
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st);
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st);
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st);
+
+// Variant reductions (variant.hip).
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
+// max_logit[h] = max over the n partials ml_part[h * n ...] (-inf when n == 0).
+hipError_t launch_max_logit_reduce(const float* ml_part, size_t n, int Hq, float* max_logit, hipStream_t st);
+// dsink[h] = sum over b, i of rows[(b * Hq + h) * Sq + i], in a fixed order.
+hipError_t launch_dsink_reduce(const float* rows, int B, int Hq, int Sq, float* dsink, hipStream_t st);
+// out[e] = sum over b < B of parts[b * n + e] in order b = 0, 1, ..., converted to the element type.
+hipError_t launch_dbias_reduce(int dtype_bf16, const float* parts, int B, size_t n, void* out, hipStream_t st);
 
 }  // namespace bps

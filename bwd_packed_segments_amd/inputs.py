@@ -188,3 +188,25 @@ def make_case(w, seed, *, with_do: bool = True):
     if with_do:
         case["do"] = normal(seed, 3, (w.B, w.Sq, w.Hq, w.Dv), w.dtype)
     return case
+
+
+def variant_inputs(w, seed, *, bias_batch=None, bias_scale=1.0, bias_neg_inf=0.0, sink=False, sink_scale=1.0):
+    """Seeded inputs of the attention variants for workload w: an additive
+    bias [bias_batch, Hq, Sq, Skv] (None when bias_batch is None) drawn from
+    N(0, bias_scale^2), rounded to the workload's dtype, with a fraction
+    bias_neg_inf of its entries set to -inf; sink logits [Hq] (fp32, None
+    unless sink) drawn from N(0, sink_scale^2).  Streams 7, 8 and 9 of the
+    seed, apart from those of make_case."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    out = {"bias": None, "sink": None}
+    if bias_batch is not None:
+        bias = normal(seed, 7, (bias_batch, w.Hq, w.Sq, w.Skv), "fp32") * np.float32(bias_scale)
+        if w.dtype == "bf16":
+            bias = bf16_round(bias)
+        if bias_neg_inf > 0:
+            bias[_stream(seed, 9).random(bias.shape) < bias_neg_inf] = -np.inf
+        out["bias"] = bias
+    if sink:
+        out["sink"] = normal(seed, 8, (w.Hq,), "fp32") * np.float32(sink_scale)
+    return out

@@ -223,6 +223,77 @@ attn_status attn_ring_bwd(const attn_desc* desc, const attn_segments* seg, int32
                           void* dq, void* dk, void* dv,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Attention variants.  The TransformerEngine page on fused attention
+ * backward sharding ("[JAX] Align fused attn backward output gradient
+ * sharding and other test strengthening") runs backward cases with a
+ * maximum-logit output and a score modification (Changes 5) and returns
+ * optional bias gradients next to the Q/K/V gradients (Diagram); the page
+ * "[JAX] Make all jax attention calls use non-packed common calls" links a
+ * change adding sink attention.  The pages do not define them; the readings
+ * taken here are:
+ *
+ *   x_ij = scale * <q_i, k_j> + bias[b', h, i, j]      (b' = b, or 0 when
+ *                                                       one slab is shared)
+ *   S_ij = softcap * tanh(x_ij / softcap) if softcap > 0, else x_ij
+ *   LSE_i = log(exp(sink[h]) + sum_{allowed j} exp(S_ij))   (no sink term
+ *           without sink logits),   P_ij = exp(S_ij - LSE_i)
+ *   max_logit[h] = max of S_ij over batch rows and allowed pairs (-inf if
+ *                  there is none; the sink is not a pair)
+ *   dS_ij = P_ij (dP_ij - Delta_i),  dx_ij = dS_ij * (1 - (S_ij/softcap)^2)
+ *           under soft-capping (dS_ij otherwise),
+ *   dQ_i = scale sum_j dx_ij k_j,  dK_j = scale sum_i dx_ij q_i,
+ *   dbias[b', h, i, j] = sum of dx_ij over the batch rows b that read slab b'
+ *                        (0 at pairs the mask removes),
+ *   dsink[h] = - sum_{b, i} exp(sink[h] - LSE_{b,h,i}) Delta_{b,h,i}.
+ *
+ * A query that attends no key has O = 0 and LSE = sink[h] (-inf without a
+ * sink).  Every field may be left zero / NULL; with nothing requested the
+ * calls are exactly attn_fwd / attn_bwd_phase.  bias (and dbias) are
+ * [bias_batch, Hq, Sq, Skv] contiguous, element type of q, 16-byte aligned,
+ * entries finite or -inf; sink, max_logit and dsink are [Hq] fp32.  All
+ * pointers are device memory owned by the caller.  dbias is written by the
+ * PREPARE (zero fill) and DKDV phases, dsink by PREPARE, max_logit by the
+ * forward; when bias_batch == 1 < B the per-row dx are summed in fp32 in
+ * batch-row order in the workspace, so dbias is bitwise reproducible too.
+ * Errors: bias_batch other than 1 or B, dbias without bias, dsink without
+ * sink, a negative or non-finite softcap are ATTN_E_INVALID; a misaligned
+ * bias / dbias is ATTN_E_UNSUPPORTED. */
+typedef struct {
+  const void* bias;        /* additive logit bias, or NULL                    */
+  int32_t bias_batch;      /* 1 (one slab for every batch row) or B           */
+  float softcap;           /* > 0: soft-capping of the logits; 0: none        */
+  const float* sink;       /* [Hq] sink logits (natural log), or NULL         */
+  float* max_logit;        /* forward output [Hq], or NULL                    */
+  void* dbias;             /* backward output, bias's shape and type, or NULL */
+  float* dsink;            /* backward output [Hq], or NULL                   */
+} attn_variant;
+
+/* Workspace bytes of the variant calls (at least the plain calls' sizes;
+ * var may be NULL).  0 for an invalid descriptor or variant. */
+size_t attn_fwd_ex_workspace_size(const attn_desc* desc, const attn_segments* seg, const attn_variant* var);
+size_t attn_bwd_ex_workspace_size(const attn_desc* desc, const attn_segments* seg, const attn_variant* var);
+
+/* attn_fwd, attn_bwd and attn_bwd_phase with the variants of var applied;
+ * same tensors, layouts, ownership, streams and errors. */
+attn_status attn_fwd_ex(const attn_desc* desc, const attn_segments* seg, const attn_variant* var,
+                        const void* q, const void* k, const void* v,
+                        void* o, float* lse,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream, int32_t* route_out);
+attn_status attn_bwd_ex(const attn_desc* desc, const attn_segments* seg, const attn_variant* var,
+                        const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream, int32_t* route_out);
+attn_status attn_bwd_ex_phase(int32_t phases, const attn_desc* desc, const attn_segments* seg,
+                              const attn_variant* var,
+                              const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dout,
+                              void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream, int32_t* route_out);
+
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* attn_last_error(void);
 

@@ -138,7 +138,7 @@ def forward_ex(q, k, v, *, causal: bool, scale=None, segments=None, heads=None, 
 
 
 def backward_ex(q, k, v, do, *, causal: bool, scale=None, segments=None, heads=None, bias=None, softcap=0.0,
-                sink=None):
+                sink=None, return_p=False):
     """Gradients of O with respect to Q, K, V, the bias and the sink logits
     for upstream dO.
 
@@ -146,7 +146,9 @@ def backward_ex(q, k, v, do, *, causal: bool, scale=None, segments=None, heads=N
     key/value head are complete only when its whole group is in the subset
     (otherwise NaN), dbias and dsink of heads outside it are NaN.  Returns
     dQ, dK, dV, dbias (bias's shape, None without bias), dsink ([Hq], None
-    without sink), and O, LSE, Delta of the heads computed.
+    without sink), and O, LSE, Delta of the heads computed (with
+    ``return_p`` also the probabilities P [B, Hq, Sq, Skv], for error
+    bounds that scale with them).
     """
     q, k, v, dims, scale, bias, softcap, sink = _prep(q, k, v, scale, bias, softcap, sink)
     B, Sq, Skv, Hq, Hkv, Dqk, Dv = dims
@@ -164,6 +166,7 @@ def backward_ex(q, k, v, do, *, causal: bool, scale=None, segments=None, heads=N
     O = np.full((B, Sq, Hq, Dv), np.nan)
     LSE = np.full((B, Hq, Sq), np.nan)
     Delta = np.full((B, Hq, Sq), np.nan)
+    Pall = np.full((B, Hq, Sq, Skv), np.nan) if return_p else None
     for h in hs:
         if dbias is not None:
             dbias[:, h] = 0.0
@@ -195,8 +198,13 @@ def backward_ex(q, k, v, do, *, causal: bool, scale=None, segments=None, heads=N
             O[b, :, h, :] = P @ vh
             LSE[b, h] = lse
             Delta[b, h] = delta
+            if return_p:
+                Pall[b, h] = P
     for c in range(Hkv):
         if c not in complete:
             dK[:, :, c, :] = np.nan
             dV[:, :, c, :] = np.nan
-    return {"dQ": dQ, "dK": dK, "dV": dV, "dbias": dbias, "dsink": dsink, "O": O, "LSE": LSE, "Delta": Delta}
+    out = {"dQ": dQ, "dK": dK, "dV": dV, "dbias": dbias, "dsink": dsink, "O": O, "LSE": LSE, "Delta": Delta}
+    if return_p:
+        out["P"] = Pall
+    return out

@@ -179,3 +179,54 @@ def test_ring_workspace_sizes():
     assert f1 >= o_bytes and f3 >= 3 * o_bytes
     assert b1 >= qkv_bytes and b3 >= 3 * qkv_bytes
     assert B.ring_workspace_sizes(d, None, 7) == (0, 0)
+
+
+def _var(**kw):
+    f = dict(bias=None, bias_batch=1, softcap=0.0, sink=None, max_logit=None, dbias=None, dsink=None)
+    f.update(kw)
+    return B.attn_variant(f["bias"], f["bias_batch"], f["softcap"], f["sink"], f["max_logit"], f["dbias"],
+                          f["dsink"])
+
+
+def test_variant_validation():
+    d = good()                                   # B = 2
+    ptr = 1 << 12
+    cases = [
+        (_var(bias=ptr, bias_batch=3), False, B.ATTN_E_INVALID, "bias_batch"),
+        (_var(bias=ptr, bias_batch=0), False, B.ATTN_E_INVALID, "bias_batch"),
+        (_var(softcap=-1.0), False, B.ATTN_E_INVALID, "softcap"),
+        (_var(softcap=float("inf")), False, B.ATTN_E_INVALID, "softcap"),
+        (_var(softcap=float("nan")), False, B.ATTN_E_INVALID, "softcap"),
+        (_var(dbias=ptr), True, B.ATTN_E_INVALID, "dbias"),
+        (_var(dsink=ptr), True, B.ATTN_E_INVALID, "dsink"),
+        (_var(bias=ptr + 2), False, B.ATTN_E_UNSUPPORTED, "aligned"),
+        (_var(bias=ptr, dbias=ptr + 8), True, B.ATTN_E_UNSUPPORTED, "aligned"),
+        (_var(sink=ptr + 2), False, B.ATTN_E_INVALID, "aligned"),
+    ]
+    for var, bwd, status, word in cases:
+        st, text = B.validate_ex(d, var, bwd=bwd)
+        assert st == status and word in text, (st, text)
+    # descriptor errors come first, and a too-small workspace is refused
+    st, text = B.validate_ex(good(Hq=6, Hkv=4), _var(softcap=1.0))
+    assert st == B.ATTN_E_INVALID and "multiple" in text
+    fwd, _ = B.ex_workspace_sizes(d, _var(max_logit=ptr))
+    st, text = B.validate_ex(d, _var(max_logit=ptr), ws=1 << 20, ws_bytes=fwd - 1)
+    assert st == B.ATTN_E_WORKSPACE
+
+
+def test_variant_workspace_sizes():
+    d = good(B=2, Sq=300, Skv=300, Hq=4, Hkv=2)
+    plain = (B.fwd_workspace_size(d), B.bwd_workspace_size(d))
+    ptr = 1 << 12
+    assert B.ex_workspace_sizes(d, None) == plain
+    assert B.ex_workspace_sizes(d, _var()) == plain
+    assert B.ex_workspace_sizes(d, _var(softcap=2.0, sink=ptr, bias=ptr, bias_batch=2)) == plain
+    f, b = B.ex_workspace_sizes(d, _var(max_logit=ptr))
+    assert f >= plain[0] + 4 * 2 * 3 * 4 * 4 and b == plain[1]        # [Hq][B][3 query tiles][4 waves] fp32
+    f, b = B.ex_workspace_sizes(d, _var(sink=ptr, dsink=ptr))
+    assert f == plain[0] and b >= plain[1] + 2 * 4 * 300 * 4          # one fp32 term per row
+    f, b = B.ex_workspace_sizes(d, _var(bias=ptr, bias_batch=1, dbias=ptr))
+    assert b >= plain[1] + 2 * 4 * 300 * 300 * 4                     # fp32 partials per batch row
+    f, b = B.ex_workspace_sizes(d, _var(bias=ptr, bias_batch=2, dbias=ptr))
+    assert b == plain[1]                                              # written in place
+    assert B.ex_workspace_sizes(d, _var(softcap=-1.0)) == (0, 0)
