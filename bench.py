@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 from bwd_packed_segments_amd import inputs  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_BYTES = 8.0e12
 PEAK_FP32_TFLOPS = 157.3
 METRIC = "fwd+bwd attention TFLOP/s (bf16) and % of MI355X MFMA peak, 1 GPU"
 DEFAULT_WORKLOAD = "gqa_causal_8k"
@@ -90,6 +91,20 @@ def flops(w, n):
     }
 
 
+def kernel_core_bytes(w):
+    """Algorithmic HBM bytes per launch of each kernel without variants:
+    every tensor it must read or write, once."""
+    es = 2 if w.dtype == "bf16" else 4
+    q = w.B * w.Sq * w.Hq * w.Dqk * es
+    o = w.B * w.Sq * w.Hq * w.Dv * es
+    k = w.B * w.Skv * w.Hkv * w.Dqk * es
+    v = w.B * w.Skv * w.Hkv * w.Dv * es
+    row = w.B * w.Hq * w.Sq * 4
+    return {"attn_fwd": q + k + v + o + row,
+            "attn_bwd_dkdv": q + o + k + v + 2 * row + k + v,
+            "attn_bwd_dq": q + o + k + v + 2 * row + q}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for fn in KERNEL_SOURCES:
@@ -114,13 +129,37 @@ def traffic_for(kernel: str, workload: str):
 
 # ------------------------------------------------------------------ GPU timing
 
-def run_gpu(w, steps, warmup, seed=0):
+VARIANT_SOFTCAP = 50.0
+
+
+def variant_tensors(w, variant, seed=0):
+    """Device inputs of the requested variants (bias [B, Hq, Sq, Skv] of the
+    workload's dtype, soft-cap value, sink logits [Hq]); seeded like the
+    rest of the inputs."""
+    import torch
+    if not variant:
+        return {}
+    if "bias" in variant and w.B * w.Hq * w.Sq * w.Skv > (1 << 30):
+        raise SystemExit(f"--variant bias: a [B, Hq, Sq, Skv] bias of {w.name} has more than 2^30 elements; "
+                         "use a smaller workload (e.g. bshd_causal_2k)")
+    vi = inputs.variant_inputs(w, seed, bias_batch=w.B if "bias" in variant else None, sink="sink" in variant)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = {"softcap": VARIANT_SOFTCAP if "softcap" in variant else 0.0, "max_logit": "max_logit" in variant}
+    out["bias"] = torch.from_numpy(vi["bias"]).to("cuda").to(dt) if vi["bias"] is not None else None
+    out["sink"] = torch.from_numpy(vi["sink"]).to("cuda") if vi["sink"] is not None else None
+    return out
+
+
+def run_gpu(w, steps, warmup, seed=0, variant=()):
     import torch
     import bwd_packed_segments_amd as bps
 
     case = inputs.make_case(w, seed)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = {k: torch.from_numpy(case[k]).to("cuda").to(dt) for k in ("q", "k", "v", "do")}
+    vt = variant_tensors(w, variant, seed)
+    fwd_var = {k: vt[k] for k in ("bias", "softcap", "sink", "max_logit")} if vt else {}
+    bwd_var = {k: vt[k] for k in ("bias", "softcap", "sink")} if vt else {}
     seg = None
     if case["segments"] is not None:
         sg = case["segments"]
@@ -128,8 +167,9 @@ def run_gpu(w, steps, warmup, seed=0):
         def t(x):
             return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
         seg = bps.Segments(t(sg["ids_q"]), t(sg.get("pos_q")), t(sg.get("ids_kv")), t(sg.get("pos_kv")))
-    fwd = bps.FwdPlan(dev["q"], dev["k"], dev["v"], causal=w.causal, segments=seg)
-    bwd = bps.BwdPlan(dev["q"], dev["k"], dev["v"], fwd.o, fwd.lse, dev["do"], causal=w.causal, segments=seg)
+    fwd = bps.FwdPlan(dev["q"], dev["k"], dev["v"], causal=w.causal, segments=seg, **fwd_var)
+    bwd = bps.BwdPlan(dev["q"], dev["k"], dev["v"], fwd.o, fwd.lse, dev["do"], causal=w.causal, segments=seg,
+                      **bwd_var)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -323,6 +363,10 @@ def main():
     ap.add_argument("--ring", type=int, default=0, metavar="CP",
                     help="time the one-GPU ring emulation with CP shards (attn_ring_fwd + attn_ring_bwd) "
                          "instead of the plain entry points; same workload and FLOP count")
+    ap.add_argument("--variant", default="",
+                    help="comma list of attention variants to run through attn_fwd_ex / attn_bwd_ex: bias "
+                         "(per-row [B, Hq, Sq, Skv] bias with its gradient), softcap (soft-capping at "
+                         f"{VARIANT_SOFTCAP:g}), sink (sink logits with their gradient), max_logit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -356,7 +400,11 @@ def main():
     if args.ring:
         ring_bench(w, args.ring, args.steps, args.warmup)
         return
-    case, wall, avg, med, route = run_gpu(w, args.steps, args.warmup)
+    variant = tuple(x for x in args.variant.split(",") if x)
+    unknown = set(variant) - {"bias", "softcap", "sink", "max_logit"}
+    if unknown:
+        raise SystemExit(f"unknown --variant entries {sorted(unknown)}")
+    case, wall, avg, med, route = run_gpu(w, args.steps, args.warmup, variant=variant)
     n = allowed_pairs(w, case["segments"])
     F = flops(w, n)
     f_step = F["fwd"] + F["bwd"]
@@ -370,8 +418,26 @@ def main():
     ms_dom, f_dom = kernels[dom]
     achieved = f_dom / (ms_dom * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, w.name), "kernel": dom,
-                "avg_ms": round(ms_dom, 4)}
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, w.name) if not variant else None,
+                "kernel": dom, "avg_ms": round(ms_dom, 4)}
+    if "bias" in variant:
+        # A bias adds one element read per allowed pair to the forward and
+        # dQ kernels, and a read plus a dbias write to dK/dV: the dominant
+        # kernel may then be bound by HBM instead of the matrix cores.
+        es = 2 if w.dtype == "bf16" else 4
+        core = kernel_core_bytes(w)
+        extra = {"attn_fwd": n * es, "attn_bwd_dq": n * es, "attn_bwd_dkdv": 2 * n * es}
+        hbm_bytes = core[dom] + extra[dom]
+        t_mfma = f_dom / (peak * 1e12)
+        t_hbm = hbm_bytes / PEAK_HBM_BYTES
+        if t_hbm > t_mfma:
+            gbs = hbm_bytes / (ms_dom * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                        "frac": round(gbs * 1e9 / PEAK_HBM_BYTES, 4), "traffic": None, "kernel": dom,
+                        "avg_ms": round(ms_dom, 4), "alg_bytes": int(hbm_bytes),
+                        "mfma_tflops": round(achieved, 2)}
+        else:
+            roofline["alg_bytes"] = int(hbm_bytes)
 
     out = {
         "metric": METRIC,
@@ -394,6 +460,11 @@ def main():
         "phase_ms_median": {k: round(v, 4) for k, v in med.items()},
         "roofline": roofline,
     }
+    if variant:
+        out["metric"] = METRIC + " (attention variants)"
+        out["config"]["variants"] = {"list": list(variant), "softcap": VARIANT_SOFTCAP if "softcap" in variant else 0,
+                                     "bias": "[B, Hq, Sq, Skv] per batch row, N(0,1)" if "bias" in variant else None}
+        args.no_cpu_baseline = True      # the baseline line is the plain workload's
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, case, f_step / w.Hq, args.cpu_seconds)
         cb.pop("seconds", None)

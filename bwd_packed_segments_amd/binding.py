@@ -279,28 +279,41 @@ def attn_bwd(q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segment
 
 class FwdPlan:
     """A forward for fixed tensors with its outputs and workspace allocated
-    once, so that repeated calls allocate nothing."""
+    once, so that repeated calls allocate nothing.  With any of bias,
+    softcap, sink or max_logit it runs attn_fwd_ex (self.max_logit holds the
+    per-head maxima when asked)."""
 
-    def __init__(self, q, k, v, *, causal=False, scale=None, segments: Segments | None = None, flags=0):
+    def __init__(self, q, k, v, *, causal=False, scale=None, segments: Segments | None = None, flags=0, bias=None,
+                 softcap=0.0, sink=None, max_logit=False):
         import torch
         _require_device(q, k, v)
         B, Sq, Hq, _ = q.shape
         self.t = (q, k, v)
         self.o = torch.empty((B, Sq, Hq, v.shape[3]), dtype=q.dtype, device=q.device)
         self.lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+        self.max_logit = torch.empty((Hq,), dtype=torch.float32, device=q.device) if max_logit else None
         self.desc = _desc_for(q, k, v, _strides(self.o), causal, scale, flags)
         self.cs, self.csp = _seg_ptr(segments)
         self.segments = segments
-        self.ws = _workspace(lib().attn_fwd_workspace_size(ctypes.byref(self.desc), self.csp), q.device)
+        self.ex = bias is not None or bool(softcap) or sink is not None or max_logit
+        self.keep = (bias, sink)
+        self.var = _variant(q, bias, softcap, sink, max_logit=self.max_logit) if self.ex else None
+        L = lib()
+        nbytes = (L.attn_fwd_ex_workspace_size(ctypes.byref(self.desc), self.csp, ctypes.byref(self.var))
+                  if self.ex else L.attn_fwd_workspace_size(ctypes.byref(self.desc), self.csp))
+        self.ws = _workspace(nbytes, q.device)
         self.route = None
 
     def run(self, stream=None):
         q, k, v = self.t
         st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(q.device)
         route = ctypes.c_int32(-1)
-        _check(lib().attn_fwd(ctypes.byref(self.desc), self.csp, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              self.o.data_ptr(), self.lse.data_ptr(), self.ws.data_ptr(), self.ws.numel(), st,
-                              ctypes.byref(route)))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), self.o.data_ptr(), self.lse.data_ptr(), self.ws.data_ptr(),
+                self.ws.numel(), st, ctypes.byref(route))
+        if self.ex:
+            _check(lib().attn_fwd_ex(ctypes.byref(self.desc), self.csp, ctypes.byref(self.var), *args))
+        else:
+            _check(lib().attn_fwd(ctypes.byref(self.desc), self.csp, *args))
         self.route = ROUTE_NAMES[route.value]
         return self.o, self.lse
 
@@ -308,10 +321,12 @@ class FwdPlan:
 class BwdPlan:
     """A backward prepared once for fixed tensors, whose phases can be
     launched separately (prepare, then dK/dV and dQ in either order or on
-    two streams).  Holds the outputs and the workspace."""
+    two streams).  Holds the outputs and the workspace.  With any of bias,
+    softcap or sink it runs attn_bwd_ex_phase and also returns dbias and
+    dsink (self.dbias, self.dsink)."""
 
     def __init__(self, q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segments | None = None,
-                 flags=0):
+                 flags=0, bias=None, softcap=0.0, sink=None):
         import torch
         _require_device(q, k, v, o, lse, do)
         if do.stride() != o.stride() or do.shape != o.shape:
@@ -323,17 +338,26 @@ class BwdPlan:
         self.desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
         self.cs, self.csp = _seg_ptr(segments)
         self.segments = segments
+        self.ex = bias is not None or bool(softcap) or sink is not None
+        self.dbias = torch.empty_like(bias) if bias is not None else None
+        self.dsink = torch.empty((q.shape[2],), dtype=torch.float32, device=q.device) if sink is not None else None
+        self.keep = (bias, sink)
+        self.var = _variant(q, bias, softcap, sink, dbias=self.dbias, dsink=self.dsink) if self.ex else None
         L = lib()
-        self.ws = _workspace(L.attn_bwd_workspace_size(ctypes.byref(self.desc), self.csp), q.device)
+        nbytes = (L.attn_bwd_ex_workspace_size(ctypes.byref(self.desc), self.csp, ctypes.byref(self.var))
+                  if self.ex else L.attn_bwd_workspace_size(ctypes.byref(self.desc), self.csp))
+        self.ws = _workspace(nbytes, q.device)
 
     def run(self, phases=ATTN_BWD_ALL, stream=None):
-        import torch
         q, k, v, o, lse, do = self.t
         st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(q.device)
-        _check(lib().attn_bwd_phase(phases, ctypes.byref(self.desc), self.csp, q.data_ptr(), k.data_ptr(),
-                                    v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), self.dq.data_ptr(),
-                                    self.dk.data_ptr(), self.dv.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
-                                    st, None))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(), self.ws.data_ptr(), self.ws.numel(), st,
+                None)
+        if self.ex:
+            _check(lib().attn_bwd_ex_phase(phases, ctypes.byref(self.desc), self.csp, ctypes.byref(self.var), *args))
+        else:
+            _check(lib().attn_bwd_phase(phases, ctypes.byref(self.desc), self.csp, *args))
         return self.dq, self.dk, self.dv
 
 

@@ -59,8 +59,8 @@ def units():
     out.append(("variant", [os.path.join(CSRC, "variant.hip")], []))
     for t, dqk, dv in INSTANCES:
         for part, tag in ((0, "fwd"), (1, "dq"), (2, "dkdv")):
-            for var in (0, 1):
-                name = f"attn_{tag}_{t}_{dqk}_{dv}" + ("_var" if var else "")
+            for var in ((0, 1, 2) if part == 0 else (0, 1)):
+                name = f"attn_{tag}_{t}_{dqk}_{dv}" + ("" if var == 0 else f"_var{var}")
                 out.append((name, [os.path.join(CSRC, "attn_inst.hip")],
                             [f"-DINST_T={t}", f"-DINST_DQK={dqk}", f"-DINST_DV={dv}", f"-DINST_PART={part}",
                              f"-DINST_VAR={var}"]))

@@ -211,20 +211,34 @@ hipError_t run_bwd_phases(int phases, const bps::BwdArgs& a, hipStream_t st) {
 }
 
 template <typename T, int DQK, int DV>
-hipError_t run_fwd(bool var, const bps::FwdArgs& a, hipStream_t st) {
-  return var ? bps::launch_fwd<T, DQK, DV, true>(a, st) : bps::launch_fwd<T, DQK, DV, false>(a, st);
+hipError_t run_fwd(int vm, const bps::FwdArgs& a, hipStream_t st) {
+  if (vm == 2) return bps::launch_fwd<T, DQK, DV, 2>(a, st);
+  if (vm == 1) return bps::launch_fwd<T, DQK, DV, 1>(a, st);
+  return bps::launch_fwd<T, DQK, DV, 0>(a, st);
 }
 
+// var_delta: the prepare kernel writes the sink-gradient terms; var_attn:
+// dK/dV and dQ apply a bias or a soft cap.  A sink alone needs neither: it
+// enters the backward only through the saved LSE.
 template <typename T, int DQK, int DV>
-hipError_t run_bwd(int phases, bool var, const bps::BwdArgs& a, hipStream_t st) {
-  return var ? run_bwd_phases<T, DQK, DV, true>(phases, a, st) : run_bwd_phases<T, DQK, DV, false>(phases, a, st);
+hipError_t run_bwd(int phases, bool var_delta, bool var_attn, const bps::BwdArgs& a, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (phases & ATTN_BWD_PREPARE) {
+    e = var_delta ? run_bwd_phases<T, DQK, DV, true>(ATTN_BWD_PREPARE, a, st)
+                  : run_bwd_phases<T, DQK, DV, false>(ATTN_BWD_PREPARE, a, st);
+    if (e != hipSuccess) return e;
+  }
+  const int rest = phases & (ATTN_BWD_DKDV | ATTN_BWD_DQ);
+  if (rest)
+    e = var_attn ? run_bwd_phases<T, DQK, DV, true>(rest, a, st) : run_bwd_phases<T, DQK, DV, false>(rest, a, st);
+  return e;
 }
 
-hipError_t dispatch_fwd(int dtype, int dqk, int dv, bool var, const bps::FwdArgs& a, hipStream_t st) {
+hipError_t dispatch_fwd(int dtype, int dqk, int dv, int vm, const bps::FwdArgs& a, hipStream_t st) {
 #define BPS_FWD_BF16(DQK, DV) \
-  if (dqk == DQK && dv == DV) return run_fwd<bps::bf16, DQK, DV>(var, a, st);
+  if (dqk == DQK && dv == DV) return run_fwd<bps::bf16, DQK, DV>(vm, a, st);
 #define BPS_FWD_FP32(DQK, DV) \
-  if (dqk == DQK && dv == DV) return run_fwd<float, DQK, DV>(var, a, st);
+  if (dqk == DQK && dv == DV) return run_fwd<float, DQK, DV>(vm, a, st);
   if (dtype == ATTN_BF16) {
     BPS_BF16_DIMS(BPS_FWD_BF16)
   } else {
@@ -235,11 +249,12 @@ hipError_t dispatch_fwd(int dtype, int dqk, int dv, bool var, const bps::FwdArgs
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_bwd(int phases, int dtype, int dqk, int dv, bool var, const bps::BwdArgs& a, hipStream_t st) {
+hipError_t dispatch_bwd(int phases, int dtype, int dqk, int dv, bool var_delta, bool var_attn,
+                        const bps::BwdArgs& a, hipStream_t st) {
 #define BPS_BWD_BF16(DQK, DV) \
-  if (dqk == DQK && dv == DV) return run_bwd<bps::bf16, DQK, DV>(phases, var, a, st);
+  if (dqk == DQK && dv == DV) return run_bwd<bps::bf16, DQK, DV>(phases, var_delta, var_attn, a, st);
 #define BPS_BWD_FP32(DQK, DV) \
-  if (dqk == DQK && dv == DV) return run_bwd<float, DQK, DV>(phases, var, a, st);
+  if (dqk == DQK && dv == DV) return run_bwd<float, DQK, DV>(phases, var_delta, var_attn, a, st);
   if (dtype == ATTN_BF16) {
     BPS_BF16_DIMS(BPS_BWD_BF16)
   } else {
@@ -490,7 +505,8 @@ attn_status fwd_impl(const attn_desc* d, const attn_segments* seg, const attn_va
     a.var = var_view(d, var, vp, ws, false);
     if (d->Sq > 0) {
       if ((st = prepare_segments(d, seg, p, ws, hs, &a.seg)) != ATTN_OK) return st;
-      hipError_t e = dispatch_fwd(d->dtype, d->Dqk, d->Dv, vp.on, a, hs);
+      const int vm = !vp.on ? 0 : (var->bias != nullptr || var->softcap > 0.f) ? 2 : 1;
+      hipError_t e = dispatch_fwd(d->dtype, d->Dqk, d->Dv, vm, a, hs);
       if (e != hipSuccess) return fail(ATTN_E_DEVICE, "forward launch: %s", hipGetErrorString(e));
     }
     if (vp.on && var->max_logit) {
@@ -554,7 +570,9 @@ attn_status bwd_impl(int32_t phases, const attn_desc* d, const attn_segments* se
     }
     if (!(d->Sq == 0 && d->Skv == 0)) {
       if ((st = prepare_segments(d, seg, p, ws, hs, &a.seg, prep)) != ATTN_OK) return st;
-      e = dispatch_bwd(phases, d->dtype, d->Dqk, d->Dv, vp.on, a, hs);
+      const bool var_attn = vp.on && (var->bias != nullptr || var->softcap > 0.f);
+      const bool var_delta = vp.on && var->dsink != nullptr;
+      e = dispatch_bwd(phases, d->dtype, d->Dqk, d->Dv, var_delta, var_attn, a, hs);
       if (e != hipSuccess) return fail(ATTN_E_DEVICE, "backward launch: %s", hipGetErrorString(e));
     }
     // Variants, after: the per-head sink gradient (from the prepare phase's

@@ -2,7 +2,8 @@
 // the build compiles this file once for every combination, with INST_T,
 // INST_DQK, INST_DV, INST_PART (0 forward, 1 Delta + dQ, 2 dK/dV) and
 // INST_VAR (0 plain kernels, 1 kernels that apply bias, soft-capping, sink
-// and max logit) set on the command line.  Keeping the kernel families apart
+// and max logit; for the forward also 2, the kernel for bias and soft-cap,
+// 1 being the one for sink and max logit alone) set on the command line.  Keeping the kernel families apart
 // also keeps the code generated for one from depending on the others.
 #include "attn_kernels.hpp"
 
@@ -12,7 +13,7 @@
 
 namespace bps {
 #if INST_PART == 0
-template hipError_t launch_fwd<INST_T, INST_DQK, INST_DV, INST_VAR != 0>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd<INST_T, INST_DQK, INST_DV, INST_VAR>(const FwdArgs&, hipStream_t);
 #elif INST_PART == 1
 template hipError_t launch_bwd_delta<INST_T, INST_DQK, INST_DV, INST_VAR != 0>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<INST_T, INST_DQK, INST_DV, INST_VAR != 0>(const BwdArgs&, hipStream_t);

@@ -118,54 +118,121 @@ __device__ inline void stage_kv_meta(const SegView& sv, int b, int Skv, int k0, 
 
 // ------------------------------------------------------------ variants
 
-// Base-2 logit of one pair under the variants: x = raw * scale + bias
-// (natural units), soft-capped to softcap * tanh(x / softcap) when a cap is
-// set, times log2(e).  tanh(y) = 1 - 2 / (exp(2y) + 1), which saturates to
-// +-1 as |y| grows, so a capped logit is always finite.
-__device__ inline float var_logit2(float raw, float bias, float scale, const VarView& v) {
-  const float x = fmaf(raw, scale, bias);
-  if (v.softcap > 0.f) {
-    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(x * v.cap_k) + 1.f);
-    return t * v.cap_l2;
-  }
-  return x * kLog2e;
-}
-
-// dS/dx at a base-2 logit s2: 1 - tanh^2 under soft-capping (tanh = s2 /
-// (softcap log2 e); a masked logit, -inf, gives 0), 1 otherwise.
-__device__ inline float var_dx_factor(float s2, const VarView& v) {
-  if (v.softcap > 0.f) {
-    const float t = s2 * v.cap_inv;
-    return fmaxf(1.f - t * t, 0.f);
-  }
-  return 1.f;
-}
-
-// Variant logits of a 32x32 tile with keys in rows (S^T in the forward and
-// dQ kernels): brow is the bias row of the lane's query (NULL: no bias, or
-// a query past Sq), the keys are kbase + rmap(hf, r).
+// Bias values of one 32x32 tile, kept in the element type until used
+// (slot r is v[r / 4][r % 4]); all zero without a bias.
 template <typename T>
-__device__ inline void var_tile_keys(f32x16& x, const VarView& v, const T* brow, int kbase, int Skv, float scale,
-                                     int hf) {
+struct BiasTile {
+  typename Elem<T>::P4 v[4];
+};
+
+// Bias of a tile with keys in rows (S^T in the forward and dQ kernels):
+// slot r holds key kbase + rmap(hf, r) of brow, the bias row of the lane's
+// query (NULL: no bias, or a query past Sq).  Slots 4g..4g+3 are four
+// consecutive keys, loaded at once when rows are aligned (Skv a multiple
+// of 4).
+template <typename T>
+__device__ inline BiasTile<T> bias_keys(const T* brow, int kbase, int Skv, int hf) {
+  using P4 = typename Elem<T>::P4;
+  BiasTile<T> b;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int j = kbase + rmap(hf, r);
-    const float bv = (brow != nullptr && j < Skv) ? (float)brow[j] : 0.f;
-    x[r] = var_logit2(x[r], bv, scale, v);
+  for (int g = 0; g < 4; ++g) b.v[g] = P4{};
+  if (brow == nullptr) return b;
+  if (kbase + 32 <= Skv && (Skv & 3) == 0) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) b.v[g] = *reinterpret_cast<const P4*>(brow + kbase + 8 * g + 4 * hf);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = kbase + rmap(hf, r);
+      if (j < Skv) b.v[r >> 2][r & 3] = brow[j];
+    }
+  }
+  return b;
+}
+
+// The same with queries in rows (S in the dK/dV kernels): slot r holds
+// query ibase + rmap(hf, r) of bcol, the bias column of the lane's key
+// (queries Skv elements apart; NULL: no bias, or a key past Skv).
+template <typename T>
+__device__ inline BiasTile<T> bias_queries(const T* bcol, int ibase, int Sq, int Skv, int hf) {
+  using P4 = typename Elem<T>::P4;
+  BiasTile<T> b;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) b.v[g] = P4{};
+  if (bcol == nullptr) return b;
+  if (ibase + 32 <= Sq) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) b.v[r >> 2][r & 3] = bcol[(size_t)(ibase + rmap(hf, r)) * Skv];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = ibase + rmap(hf, r);
+      if (i < Sq) b.v[r >> 2][r & 3] = bcol[(size_t)i * Skv];
+    }
+  }
+  return b;
+}
+
+// Raw scores of a tile -> base-2 variant logits, in place: x = raw * scale
+// + bias (natural units), soft-capped to softcap * tanh(x / softcap) when a
+// cap is set, times log2(e).  tanh(y) = 1 - 2 / (exp(2y) + 1), which
+// saturates to +-1 as |y| grows, so a capped logit is always finite.  The
+// branch is uniform, taken once per tile.
+template <typename T>
+__device__ inline void var_logits(f32x16& x, const BiasTile<T>& bias, const VarView& v, float scale) {
+  if (v.softcap > 0.f) {
+    const float sk = scale * v.cap_k;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float bk = static_cast<float>(bias.v[r >> 2][r & 3]) * v.cap_k;
+      const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(fmaf(x[r], sk, bk)) + 1.f);
+      x[r] = t * v.cap_l2;
+    }
+  } else {
+    const float sl2 = scale * kLog2e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = fmaf(x[r], sl2, static_cast<float>(bias.v[r >> 2][r & 3]) * kLog2e);
   }
 }
 
-// The same with queries in rows (S in the dK/dV kernels): bcol is the bias
-// column of the lane's key (queries Skv elements apart; NULL: no bias, or a
-// key past Skv), the queries are ibase + rmap(hf, r).
-template <typename T>
-__device__ inline void var_tile_queries(f32x16& x, const VarView& v, const T* bcol, int ibase, int Sq, int Skv,
-                                        float scale, int hf) {
+// dS/dx at a base-2 logit s2 under soft-capping: 1 - tanh^2, with tanh =
+// s2 / (softcap log2 e); a masked logit (-inf) gives 0.
+__device__ inline float softcap_dx(float s2, const VarView& v) {
+  const float t = s2 * v.cap_inv;
+  return fmaxf(1.f - t * t, 0.f);
+}
+
+// Softmax gradient of a dK/dV tile (queries in rows) from base-2 variant
+// logits sa and dP in pa: sa <- P = exp2(sa - LSE2), pa <- dLoss/dx =
+// P (dP - Delta) dS/dx; lse2 and delta are the tile's 32 rows in LDS.  The
+// soft-cap branch is uniform, taken once per tile.
+__device__ inline void var_softgrad(f32x16& sa, f32x16& pa, const float* lse2, const float* delta, const VarView& v,
+                                    int hf) {
+  if (v.softcap > 0.f) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = ibase + rmap(hf, r);
-    const float bv = (bcol != nullptr && i < Sq) ? (float)bcol[(size_t)i * Skv] : 0.f;
-    x[r] = var_logit2(x[r], bv, scale, v);
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * grp + 4 * hf);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(delta + 8 * grp + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        const float s2 = sa[r];
+        sa[r] = fast_exp2(s2 - l4[i]);
+        pa[r] = sa[r] * (pa[r] - d4[i]) * softcap_dx(s2, v);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * grp + 4 * hf);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(delta + 8 * grp + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        sa[r] = fast_exp2(sa[r] - l4[i]);
+        pa[r] = sa[r] * (pa[r] - d4[i]);
+      }
+    }
   }
 }
 
@@ -205,9 +272,13 @@ struct FwdCfg {
   static constexpr int WAVES_PER_EU = Staging<T, STAGE_BYTES>::WAVES_PER_EU;
 };
 
-template <typename T, int DQK, int DV, bool VAR>
+// VM: 0 plain; 1 sink and max logit only (scores stay raw); 2 any variant,
+// with the scores turned into bias / soft-cap logits.
+template <typename T, int DQK, int DV, int VM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, DQK, DV>::WAVES_PER_EU)))
     attn_fwd_kernel(FwdArgs a) {
+  constexpr bool VAR = VM != 0;      // sink, max logit
+  constexpr bool XFORM = VM == 2;    // bias, soft cap
   using C = FwdCfg<T, DQK, DV>;
   using E = Elem<T>;
   using F8 = typename E::F8;
@@ -296,14 +367,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
     if (general) stage_kv_meta<BN>(a.seg, b, s.Skv, k0, kid, tid, nvalid == BN);
   };
 
-  // Without variants the scores stay raw (c2 folds in the scale); with
-  // them they are turned into base-2 logits first (c2 = 1).
-  const float c2 = VAR ? 1.f : s.scale_log2;
+  // The scores stay raw (c2 folds in the scale) unless a bias or a soft cap
+  // changes them; then they are turned into base-2 logits first (c2 = 1).
+  const float c2 = XFORM ? 1.f : s.scale_log2;
   float m = -INFINITY;   // reference max of the scores (rescaled lazily)
   float l = 0.f;         // this lane half's partial sum of exp2((s - m) * c2)
-  float mxe = -INFINITY; // exact max of this query's allowed logits (base 2)
+  float mxe = -INFINITY; // exact max of this query's allowed scores
   const T* brow = nullptr;
-  if constexpr (VAR) {
+  if constexpr (XFORM) {
     if (a.var.bias != nullptr && qi < s.Sq)
       brow = static_cast<const T*>(a.var.bias) + b * a.var.bias_b + ((size_t)h * s.Sq + qi) * s.Skv;
   }
@@ -335,9 +406,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
         sacc[blk] = mma(frag_row<T, DQK>(Ks, blk * 32 + n, 16 * t + 8 * hf), qf[t], sacc[blk]);
-    if constexpr (VAR) {
+    if constexpr (XFORM) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) var_tile_keys<T>(sacc[blk], a.var, brow, k0 + blk * 32, s.Skv, s.scale, hf);
+      for (int blk = 0; blk < 2; ++blk)
+        var_logits<T>(sacc[blk], bias_keys<T>(brow, k0 + blk * 32, s.Skv, hf), a.var, s.scale);
     }
 
     if (cls == kTilePart) {
@@ -405,16 +477,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
   float inv = lt > 0.f ? 1.f / lt : 0.f;
   float lse = lt > 0.f ? m * s.scale + logf(lt) : -INFINITY;
   if constexpr (VAR) {
-    // m is a base-2 logit here.  The sink adds exp2(sink2 - m) to the sum
-    // of terms; the reference moves to the larger of the two so that no
-    // term overflows.  A row with no allowed key then has O = 0 and
-    // LSE = sink.
-    float ref = m, tot = lt, alpha = 1.f;
+    // In base-2 units the reference is m * c2.  The sink adds
+    // exp2(sink2 - ref) to the sum of terms; the reference moves to the
+    // larger of the two so that no term overflows.  A row with no allowed
+    // key then has O = 0 and LSE = sink.
+    const float m2 = m * c2;
+    float ref = m2, tot = lt, alpha = 1.f;
     if (a.var.sink != nullptr) {
       const float s2 = a.var.sink[h] * kLog2e;
       if (lt > 0.f) {
-        ref = fmaxf(m, s2);
-        alpha = fast_exp2(m - ref);
+        ref = fmaxf(m2, s2);
+        alpha = fast_exp2(m2 - ref);
         tot = lt * alpha + fast_exp2(s2 - ref);
       } else {
         ref = s2;
@@ -428,7 +501,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
       float wm = qi < s.Sq ? mxe : -INFINITY;
 #pragma unroll
       for (int d = 1; d < 32; d <<= 1) wm = fmaxf(wm, __shfl_xor(wm, d));
-      if (lane == 0) a.var.ml_part[(((size_t)h * s.B + b) * n_qt + qt) * 4 + wave] = wm * kLn2;
+      if (lane == 0) a.var.ml_part[(((size_t)h * s.B + b) * n_qt + qt) * 4 + wave] = wm * (c2 * kLn2);
     }
   }
   if (qi < s.Sq) {
@@ -640,13 +713,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<
       if constexpr (VAR) {
         // Variant logits, masked to -inf, then P and dLoss/dx = P (dP -
         // Delta) dS/dx in one pass.
-        var_tile_keys<T>(sacc, a.var, brow, k0 + blk * 32, s.Skv, s.scale, hf);
+        var_logits<T>(sacc, bias_keys<T>(brow, k0 + blk * 32, s.Skv, hf), a.var, s.scale);
         if (cls == kTilePart)
           mask_tile<true>(sacc, -INFINITY, route, causal, s.Skv, qi, qm, k0 + blk * 32, hf, kid, kid + BN, blk * 32);
+        if (a.var.softcap > 0.f) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float s2 = sacc[r];
-          sacc[r] = fast_exp2(s2 - lse2) * (pacc[r] - delta) * var_dx_factor(s2, a.var);
+          for (int r = 0; r < 16; ++r) {
+            const float s2 = sacc[r];
+            sacc[r] = fast_exp2(s2 - lse2) * (pacc[r] - delta) * softcap_dx(s2, a.var);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(sacc[r] - lse2) * (pacc[r] - delta);
         }
       } else {
         // P = exp2(S * scale * log2e - LSE2); dS = P * (dP - Delta).
@@ -868,7 +946,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
       dcol = b * a.var.dbias_b + col;
     }
 
-    auto sdp = [&](int qb, f32x16& sa, f32x16& pa) {
+    auto sdp = [&](int qb, f32x16& sa, f32x16& pa, BiasTile<T>& bq) {
+      if constexpr (VAR) bq = bias_queries<T>(bcol, i0 + qb * 32, s.Sq, s.Skv, hf);   // in flight under the products
       F8 qa[DQK / 16], da[DV / 16];
 #pragma unroll
       for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
@@ -883,24 +962,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
     };
     // P = exp2(S * scale * log2e - LSE2), dS = P * (dP - Delta); returns the
     // bf16 operands of the dV and dK products.
-    auto softgrad = [&](int qb, f32x16& sa, f32x16& pa, F8* pf, F8* dsf) {
+    auto softgrad = [&](int qb, f32x16& sa, f32x16& pa, const BiasTile<T>& bq, F8* pf, F8* dsf) {
       if constexpr (VAR) {
         // Variant logits, masked to -inf, then P and dLoss/dx = P (dP -
         // Delta) dS/dx in one pass; dx also goes to the dbias target.
-        var_tile_queries<T>(sa, a.var, bcol, i0 + qb * 32, s.Sq, s.Skv, s.scale, hf);
+        var_logits<T>(sa, bq, a.var, s.scale);
         if (part) mask_tile<false>(sa, -INFINITY, route, causal, s.Skv, kj, km, i0 + qb * 32, hf, qma, qmb, qb * 32);
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * grp + i;
-            const float s2 = sa[r];
-            sa[r] = fast_exp2(s2 - l4[i]);
-            pa[r] = sa[r] * (pa[r] - d4[i]) * var_dx_factor(s2, a.var);
-          }
-        }
+        var_softgrad(sa, pa, lse2s + qb * 32, deltas + qb * 32, a.var, hf);
         if (a.var.dbias != nullptr && kj < s.Skv) var_store_dx<T>(pa, a.var, dcol, i0 + qb * 32, s.Sq, s.Skv, hf);
       } else {
 #pragma unroll
@@ -938,17 +1006,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
 
     f32x16 s0, p0;
     F8 pf0[2], dsf0[2];
-    sdp(0, s0, p0);
+    BiasTile<T> b0;
+    sdp(0, s0, p0, b0);
     if constexpr (NQB == 2) {
       f32x16 s1, p1;
       F8 pf1[2], dsf1[2];
-      sdp(1, s1, p1);
-      softgrad(0, s0, p0, pf0, dsf0);
+      BiasTile<T> b1;
+      sdp(1, s1, p1, b1);
+      softgrad(0, s0, p0, b0, pf0, dsf0);
       dvdk(0, pf0, dsf0);
-      softgrad(1, s1, p1, pf1, dsf1);
+      softgrad(1, s1, p1, b1, pf1, dsf1);
       dvdk(1, pf1, dsf1);
     } else {
-      softgrad(0, s0, p0, pf0, dsf0);
+      softgrad(0, s0, p0, b0, pf0, dsf0);
       dvdk(0, pf0, dsf0);
     }
   };
@@ -1189,6 +1259,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     const float* deltas = lse2s + BM;
     const int* qma = reinterpret_cast<const int*>(lse2s + 2 * BM);
     const int* qmb = qma + BM;
+    // Variants: this phase's bias goes in flight before the products.
+    int ib = 0;
+    size_t col = 0;
+    BiasTile<T> bq;
+    if constexpr (VAR) {
+      ib = tile_of(x) * BM + qb * 32;
+      col = (size_t)(hkv * g + x % g) * s.Sq * s.Skv + kj;
+      const T* bcol = (a.var.bias != nullptr && kj < s.Skv)
+                          ? static_cast<const T*>(a.var.bias) + b * a.var.bias_b + col : nullptr;
+      bq = bias_queries<T>(bcol, ib, s.Sq, s.Skv, hf);
+    }
     F8 qa[DQK / 16], da[DV / 16];
 #pragma unroll
     for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
@@ -1202,24 +1283,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     if constexpr (VAR) {
       // Variant logits, masked to -inf, then P and dLoss/dx = P (dP - Delta)
       // dS/dx in one pass; dx also goes to the dbias target.
-      const int ib = tile_of(x) * BM + qb * 32;
-      const size_t col = (size_t)(hkv * g + x % g) * s.Sq * s.Skv + kj;
-      const T* bcol = (a.var.bias != nullptr && kj < s.Skv)
-                          ? static_cast<const T*>(a.var.bias) + b * a.var.bias_b + col : nullptr;
-      var_tile_queries<T>(sa, a.var, bcol, ib, s.Sq, s.Skv, s.scale, hf);
+      var_logits<T>(sa, bq, a.var, s.scale);
       if (part) mask_tile<false>(sa, -INFINITY, route, causal, s.Skv, kj, km, ib, hf, qma, qmb, qb * 32);
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * grp + i;
-          const float s2 = sa[r];
-          sa[r] = fast_exp2(s2 - l4[i]);
-          pa[r] = sa[r] * (pa[r] - d4[i]) * var_dx_factor(s2, a.var);
-        }
-      }
+      var_softgrad(sa, pa, lse2s + qb * 32, deltas + qb * 32, a.var, hf);
       if (a.var.dbias != nullptr && kj < s.Skv) var_store_dx<T>(pa, a.var, b * a.var.dbias_b + col, ib, s.Sq, s.Skv, hf);
     } else {
 #pragma unroll
@@ -1360,13 +1426,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 
 // ------------------------------------------------------------ launchers
 
-template <typename T, int DQK, int DV, bool VAR>
+template <typename T, int DQK, int DV, int VM>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<T, DQK, DV>;
   const int n_qt = (a.s.Sq + C::BM - 1) / C::BM;
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(C::THREADS), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, VM>), dim3((unsigned)nblocks), dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
 }
 

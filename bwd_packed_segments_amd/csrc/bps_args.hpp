@@ -135,8 +135,9 @@ hipError_t launch_ring_reduce(int dtype_bf16, const RingReduceArgs& a, hipStream
 hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st);
 hipError_t launch_debug_mask(const MaskArgs& a, hipStream_t st);
 
-// VAR selects the kernels that apply the variants of VarView.
-template <typename T, int DQK, int DV, bool VAR>
+// VAR / VM select the kernels that apply the variants of VarView (forward
+// VM: 0 plain, 1 sink and max logit only, 2 bias or soft cap as well).
+template <typename T, int DQK, int DV, int VM>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st);
