@@ -260,26 +260,33 @@ __device__ inline void var_store_dx(const f32x16& dx, const VarView& v, size_t c
 
 // ------------------------------------------------------------ forward
 
-template <typename T, int DQK, int DV>
+// W waves of 32 queries each.  Four waves (two workgroups per CU) by
+// default; eight (one workgroup per CU, each key/value tile loaded once for
+// 256 queries, half the load instructions per product) for bf16 without
+// segment metadata or causal mask, where wide query tiles cost no extra
+// masked work (measured: 4 % less forward time on an 18,900 x 75,600
+// shard, but 4-8 % more on the 8K causal workload).
+template <typename T, int DQK, int DV, int W = 4>
 struct FwdCfg {
-  static constexpr int BM = 128;
+  static constexpr int BM = 32 * W;
   static constexpr int BN = 64;
-  static constexpr int THREADS = 256;
+  static constexpr int THREADS = 64 * W;
   static constexpr int K_BYTES = BN * DQK * (int)sizeof(T);
   static constexpr int V_BYTES = BN * DV * (int)sizeof(T);
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES + 2 * BN * 4;
-  static constexpr int NBUF = Staging<T, STAGE_BYTES>::NBUF;
-  static constexpr int WAVES_PER_EU = Staging<T, STAGE_BYTES>::WAVES_PER_EU;
+  static constexpr int NBUF = W == 8 ? 2 : Staging<T, STAGE_BYTES>::NBUF;
+  static constexpr int WAVES_PER_EU = W == 8 ? 2 : Staging<T, STAGE_BYTES>::WAVES_PER_EU;
+  static constexpr bool WIDE_OK = sizeof(T) == 2 && 2 * STAGE_BYTES <= 160 * 1024;
 };
 
 // VM: 0 plain; 1 sink and max logit only (scores stay raw); 2 any variant,
 // with the scores turned into bias / soft-cap logits.
-template <typename T, int DQK, int DV, int VM>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, DQK, DV>::WAVES_PER_EU)))
+template <typename T, int DQK, int DV, int VM, int W = 4>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, DQK, DV, W>::WAVES_PER_EU)))
     attn_fwd_kernel(FwdArgs a) {
   constexpr bool VAR = VM != 0;      // sink, max logit
   constexpr bool XFORM = VM == 2;    // bias, soft cap
-  using C = FwdCfg<T, DQK, DV>;
+  using C = FwdCfg<T, DQK, DV, W>;
   using E = Elem<T>;
   using F8 = typename E::F8;
   constexpr int BM = C::BM, BN = C::BN;
@@ -339,7 +346,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
   __shared__ unsigned char cls_tab[kClassCap];
   const bool tabled = route != kRouteDense;
   if (tabled) {
-    fill_classes(cls_tab, t_hi - t_lo, tid, 256, [&](int i) { return classify(t_lo + i); });
+    fill_classes(cls_tab, t_hi - t_lo, tid, C::THREADS, [&](int i) { return classify(t_lo + i); });
     __syncthreads();
   }
   auto next_tile = [&](int kt, int& cls) -> int {
@@ -358,11 +365,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg
     const int k0 = kt * BN;
     const int nvalid = min(BN, s.Skv - k0);
     if (nvalid == BN) {
-      TileLoad<T, BN, DQK, 256>::direct(kp + k0 * a.sk.t, a.sk.t, Ks, tid);
-      TileLoad<T, BN, DV, 256>::direct(vp + k0 * a.sv.t, a.sv.t, Vs, tid);
+      TileLoad<T, BN, DQK, C::THREADS>::direct(kp + k0 * a.sk.t, a.sk.t, Ks, tid);
+      TileLoad<T, BN, DV, C::THREADS>::direct(vp + k0 * a.sv.t, a.sv.t, Vs, tid);
     } else {
-      TileLoad<T, BN, DQK, 256>::staged(kp + k0 * a.sk.t, a.sk.t, nvalid, Ks, tid);
-      TileLoad<T, BN, DV, 256>::staged(vp + k0 * a.sv.t, a.sv.t, nvalid, Vs, tid);
+      TileLoad<T, BN, DQK, C::THREADS>::staged(kp + k0 * a.sk.t, a.sk.t, nvalid, Ks, tid);
+      TileLoad<T, BN, DV, C::THREADS>::staged(vp + k0 * a.sv.t, a.sv.t, nvalid, Vs, tid);
     }
     if (general) stage_kv_meta<BN>(a.seg, b, s.Skv, k0, kid, tid, nvalid == BN);
   };
@@ -1432,6 +1439,14 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   const int n_qt = (a.s.Sq + C::BM - 1) / C::BM;
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
+  if constexpr (VM == 0 && FwdCfg<T, DQK, DV, 8>::WIDE_OK) {
+    if (!a.s.has_meta && !a.s.causal) {
+      using C8 = FwdCfg<T, DQK, DV, 8>;
+      const long long nb8 = (long long)a.s.B * a.s.Hq * ((a.s.Sq + C8::BM - 1) / C8::BM);
+      hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, 0, 8>), dim3((unsigned)nb8), dim3(C8::THREADS), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, VM>), dim3((unsigned)nblocks), dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
 }
