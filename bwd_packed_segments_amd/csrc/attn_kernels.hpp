@@ -571,23 +571,28 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ backward: dQ
 
-template <typename T, int DQK, int DV>
+// W waves of 32 queries each, as for the forward: eight (256-query tiles,
+// one workgroup per CU) for bf16 without metadata or causal mask.
+template <typename T, int DQK, int DV, int W = 4>
 struct DqCfg {
-  static constexpr int BM = 128;
+  static constexpr int BM = 32 * W;
   static constexpr int BN = 64;
+  static constexpr int THREADS = 64 * W;
   static constexpr int K_BYTES = BN * DQK * (int)sizeof(T);
   static constexpr int V_BYTES = BN * DV * (int)sizeof(T);
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES + 2 * BN * 4;
-  static constexpr int NBUF = Staging<T, STAGE_BYTES>::NBUF;
+  static constexpr int NBUF = W == 8 ? 2 : Staging<T, STAGE_BYTES>::NBUF;
   // Q, dO fragments and the dQ accumulator outgrow half the register file
   // for wide heads.
-  static constexpr int WAVES_PER_EU = (DQK > 128 || DQK + DV > 256) ? 1 : Staging<T, STAGE_BYTES>::WAVES_PER_EU;
+  static constexpr int WAVES_PER_EU =
+      (DQK > 128 || DQK + DV > 256) ? 1 : (W == 8 ? 2 : Staging<T, STAGE_BYTES>::WAVES_PER_EU);
+  static constexpr bool WIDE_OK = sizeof(T) == 2 && DQK <= 128 && DQK + DV <= 256 && 2 * STAGE_BYTES <= 160 * 1024;
 };
 
-template <typename T, int DQK, int DV, bool VAR>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, DQK, DV>::WAVES_PER_EU)))
+template <typename T, int DQK, int DV, bool VAR, int W = 4>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqCfg<T, DQK, DV, W>::WAVES_PER_EU)))
     attn_bwd_dq_kernel(BwdArgs a) {
-  using C = DqCfg<T, DQK, DV>;
+  using C = DqCfg<T, DQK, DV, W>;
   using E = Elem<T>;
   using F8 = typename E::F8;
   constexpr int BM = C::BM, BN = C::BN;
@@ -654,7 +659,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<
   __shared__ unsigned char cls_tab[kClassCap];
   const bool tabled = route != kRouteDense;
   if (tabled) {
-    fill_classes(cls_tab, t_hi - t_lo, tid, 256, [&](int i) { return classify(t_lo + i); });
+    fill_classes(cls_tab, t_hi - t_lo, tid, C::THREADS, [&](int i) { return classify(t_lo + i); });
     __syncthreads();
   }
   auto next_tile = [&](int kt, int& cls) -> int {
@@ -673,11 +678,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<
     const int k0 = kt * BN;
     const int nvalid = min(BN, s.Skv - k0);
     if (nvalid == BN) {
-      TileLoad<T, BN, DQK, 256>::direct(kp + k0 * a.sk.t, a.sk.t, Ks, tid);
-      TileLoad<T, BN, DV, 256>::direct(vp + k0 * a.sv.t, a.sv.t, Vs, tid);
+      TileLoad<T, BN, DQK, C::THREADS>::direct(kp + k0 * a.sk.t, a.sk.t, Ks, tid);
+      TileLoad<T, BN, DV, C::THREADS>::direct(vp + k0 * a.sv.t, a.sv.t, Vs, tid);
     } else {
-      TileLoad<T, BN, DQK, 256>::staged(kp + k0 * a.sk.t, a.sk.t, nvalid, Ks, tid);
-      TileLoad<T, BN, DV, 256>::staged(vp + k0 * a.sv.t, a.sv.t, nvalid, Vs, tid);
+      TileLoad<T, BN, DQK, C::THREADS>::staged(kp + k0 * a.sk.t, a.sk.t, nvalid, Ks, tid);
+      TileLoad<T, BN, DV, C::THREADS>::staged(vp + k0 * a.sv.t, a.sv.t, nvalid, Vs, tid);
     }
     if (general) stage_kv_meta<BN>(a.seg, b, s.Skv, k0, kid, tid, nvalid == BN);
   };
@@ -1479,6 +1484,14 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   const int n_qt = (a.s.Sq + DqCfg<T, DQK, DV>::BM - 1) / DqCfg<T, DQK, DV>::BM;
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
+  if constexpr (!VAR && DqCfg<T, DQK, DV, 8>::WIDE_OK) {
+    if (!a.s.has_meta && !a.s.causal) {
+      using C8 = DqCfg<T, DQK, DV, 8>;
+      const long long nb8 = (long long)a.s.B * a.s.Hq * ((a.s.Sq + C8::BM - 1) / C8::BM);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV, false, 8>), dim3((unsigned)nb8), dim3(C8::THREADS), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
