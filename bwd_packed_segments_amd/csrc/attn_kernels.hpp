@@ -260,15 +260,19 @@ __device__ inline void var_store_dx(const f32x16& dx, const VarView& v, size_t c
 
 // ------------------------------------------------------------ forward
 
-// W waves of 32 queries each.  Four waves (two workgroups per CU) by
-// default; eight (one workgroup per CU, each key/value tile loaded once for
-// 256 queries, half the load instructions per product) for bf16 without
-// segment metadata or causal mask, where wide query tiles cost no extra
-// masked work (measured: 4 % less forward time on an 18,900 x 75,600
+// W waves of 32 queries each, over HP query heads of one GQA group (W / HP
+// waves per head).  Four waves and one head (two workgroups per CU) by
+// default.  Eight waves load each key/value tile once for twice the
+// queries, which halves the load instructions per product: as two heads of
+// a GQA group over the same 128 queries (the masks are those of one head),
+// or, without a group to share, as one head over 256 queries for bf16
+// without segment metadata or causal mask, where wide query tiles cost no
+// extra masked work (measured: 4 % less forward time on an 18,900 x 75,600
 // shard, but 4-8 % more on the 8K causal workload).
-template <typename T, int DQK, int DV, int W = 4>
+template <typename T, int DQK, int DV, int W = 4, int HP = 1>
 struct FwdCfg {
-  static constexpr int BM = 32 * W;
+  static constexpr int QW = W / HP;     // waves per head
+  static constexpr int BM = 32 * QW;
   static constexpr int BN = 64;
   static constexpr int THREADS = 64 * W;
   static constexpr int K_BYTES = BN * DQK * (int)sizeof(T);
@@ -281,30 +285,30 @@ struct FwdCfg {
 
 // VM: 0 plain; 1 sink and max logit only (scores stay raw); 2 any variant,
 // with the scores turned into bias / soft-cap logits.
-template <typename T, int DQK, int DV, int VM, int W = 4>
-__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, DQK, DV, W>::WAVES_PER_EU)))
+template <typename T, int DQK, int DV, int VM, int W = 4, int HP = 1>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, DQK, DV, W, HP>::WAVES_PER_EU)))
     attn_fwd_kernel(FwdArgs a) {
   constexpr bool VAR = VM != 0;      // sink, max logit
   constexpr bool XFORM = VM == 2;    // bias, soft cap
-  using C = FwdCfg<T, DQK, DV, W>;
+  using C = FwdCfg<T, DQK, DV, W, HP>;
   using E = Elem<T>;
   using F8 = typename E::F8;
-  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int BM = C::BM, BN = C::BN, QW = C::QW;
   __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE_BYTES];
 
   const AttnShape& s = a.s;
   const bool causal = s.causal != 0;
   const int n_qt = (s.Sq + BM - 1) / BM;
   const int g = s.Hq / s.Hkv;
-  const int nblocks = s.B * s.Hq * n_qt;
+  const int ngh = g / HP;            // head groups of HP per KV head
+  const int nblocks = s.B * s.Hkv * ngh * n_qt;
   int L = logical_block(nblocks, s.reverse);
-  const int hg = L % g;
-  L /= g;
+  const int hgp = L % ngh;
+  L /= ngh;
   const int qrank = L % n_qt;
   L /= n_qt;
   const int hkv = L % s.Hkv;
   const int b = L / s.Hkv;
-  const int h = hkv * g + hg;
   const int qt = causal ? (n_qt - 1 - qrank) : qrank;
   const int q0 = qt * BM;
 
@@ -313,7 +317,9 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(Fwd
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hf = lane >> 5;
-  const int qi = q0 + wave * 32 + n;
+  const int h = hkv * g + hgp * HP + wave / QW;   // this wave's query head
+  const int wq = wave % QW;                        // this wave's 32 rows of the tile
+  const int qi = q0 + wq * 32 + n;
 
   const T* qp = static_cast<const T*>(a.q) + b * a.sq.b + h * a.sq.h;
   const T* kp = static_cast<const T*>(a.k) + b * a.sk.b + hkv * a.sk.h;
@@ -508,7 +514,7 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(Fwd
       float wm = qi < s.Sq ? mxe : -INFINITY;
 #pragma unroll
       for (int d = 1; d < 32; d <<= 1) wm = fmaxf(wm, __shfl_xor(wm, d));
-      if (lane == 0) a.var.ml_part[(((size_t)h * s.B + b) * n_qt + qt) * 4 + wave] = wm * (c2 * kLn2);
+      if (lane == 0) a.var.ml_part[(((size_t)h * s.B + b) * n_qt + qt) * 4 + wq] = wm * (c2 * kLn2);
     }
   }
   if (qi < s.Sq) {
@@ -571,11 +577,13 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ backward: dQ
 
-// W waves of 32 queries each, as for the forward: eight (256-query tiles,
-// one workgroup per CU) for bf16 without metadata or causal mask.
-template <typename T, int DQK, int DV, int W = 4>
+// W waves of 32 queries each over HP query heads, as for the forward:
+// eight waves as two heads of a GQA group, or as 256-query tiles of one
+// head for bf16 without metadata or causal mask.
+template <typename T, int DQK, int DV, int W = 4, int HP = 1>
 struct DqCfg {
-  static constexpr int BM = 32 * W;
+  static constexpr int QW = W / HP;
+  static constexpr int BM = 32 * QW;
   static constexpr int BN = 64;
   static constexpr int THREADS = 64 * W;
   static constexpr int K_BYTES = BN * DQK * (int)sizeof(T);
@@ -589,28 +597,28 @@ struct DqCfg {
   static constexpr bool WIDE_OK = sizeof(T) == 2 && DQK <= 128 && DQK + DV <= 256 && 2 * STAGE_BYTES <= 160 * 1024;
 };
 
-template <typename T, int DQK, int DV, bool VAR, int W = 4>
-__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqCfg<T, DQK, DV, W>::WAVES_PER_EU)))
+template <typename T, int DQK, int DV, bool VAR, int W = 4, int HP = 1>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqCfg<T, DQK, DV, W, HP>::WAVES_PER_EU)))
     attn_bwd_dq_kernel(BwdArgs a) {
-  using C = DqCfg<T, DQK, DV, W>;
+  using C = DqCfg<T, DQK, DV, W, HP>;
   using E = Elem<T>;
   using F8 = typename E::F8;
-  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int BM = C::BM, BN = C::BN, QW = C::QW;
   __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE_BYTES];
 
   const AttnShape& s = a.s;
   const bool causal = s.causal != 0;
   const int n_qt = (s.Sq + BM - 1) / BM;
   const int g = s.Hq / s.Hkv;
-  const int nblocks = s.B * s.Hq * n_qt;
+  const int ngh = g / HP;            // head groups of HP per KV head
+  const int nblocks = s.B * s.Hkv * ngh * n_qt;
   int L = logical_block(nblocks, s.reverse);
-  const int hg = L % g;
-  L /= g;
+  const int hgp = L % ngh;
+  L /= ngh;
   const int qrank = L % n_qt;
   L /= n_qt;
   const int hkv = L % s.Hkv;
   const int b = L / s.Hkv;
-  const int h = hkv * g + hg;
   const int qt = causal ? (n_qt - 1 - qrank) : qrank;
   const int q0 = qt * BM;
 
@@ -619,7 +627,8 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqC
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hf = lane >> 5;
-  const int qi = q0 + wave * 32 + n;
+  const int h = hkv * g + hgp * HP + wave / QW;   // this wave's query head
+  const int qi = q0 + (wave % QW) * 32 + n;
 
   const T* qp = static_cast<const T*>(a.q) + b * a.sq.b + h * a.sq.h;
   const T* dop = static_cast<const T*>(a.dout) + b * a.so.b + h * a.so.h;
@@ -1438,6 +1447,16 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 
 // ------------------------------------------------------------ launchers
 
+// Head pairs (GQA) in the forward and dQ; BPS_HEAD_PAIRS=0 in the
+// environment keeps one head per workgroup (for comparison).
+inline bool fwd_head_pairs() {
+  static const bool on = [] {
+    const char* e = getenv("BPS_HEAD_PAIRS");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
 template <typename T, int DQK, int DV, int VM>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<T, DQK, DV>;
@@ -1445,6 +1464,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
   if constexpr (VM == 0 && FwdCfg<T, DQK, DV, 8>::WIDE_OK) {
+    if ((a.s.Hq / a.s.Hkv) % 2 == 0 && fwd_head_pairs()) {
+      using C8 = FwdCfg<T, DQK, DV, 8, 2>;
+      const long long nb8 = (long long)a.s.B * (a.s.Hq / 2) * ((a.s.Sq + C8::BM - 1) / C8::BM);
+      hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, 0, 8, 2>), dim3((unsigned)nb8), dim3(C8::THREADS), 0, st, a);
+      return hipGetLastError();
+    }
     if (!a.s.has_meta && !a.s.causal) {
       using C8 = FwdCfg<T, DQK, DV, 8>;
       const long long nb8 = (long long)a.s.B * a.s.Hq * ((a.s.Sq + C8::BM - 1) / C8::BM);
@@ -1485,6 +1510,13 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
   if constexpr (!VAR && DqCfg<T, DQK, DV, 8>::WIDE_OK) {
+    if ((a.s.Hq / a.s.Hkv) % 2 == 0 && fwd_head_pairs()) {
+      using C8 = DqCfg<T, DQK, DV, 8, 2>;
+      const long long nb8 = (long long)a.s.B * (a.s.Hq / 2) * ((a.s.Sq + C8::BM - 1) / C8::BM);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV, false, 8, 2>), dim3((unsigned)nb8), dim3(C8::THREADS), 0, st,
+                         a);
+      return hipGetLastError();
+    }
     if (!a.s.has_meta && !a.s.causal) {
       using C8 = DqCfg<T, DQK, DV, 8>;
       const long long nb8 = (long long)a.s.B * a.s.Hq * ((a.s.Sq + C8::BM - 1) / C8::BM);
