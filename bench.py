@@ -150,7 +150,7 @@ def variant_tensors(w, variant, seed=0):
     return out
 
 
-def run_gpu(w, steps, warmup, seed=0, variant=()):
+def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
     import torch
     import bwd_packed_segments_amd as bps
 
@@ -169,7 +169,7 @@ def run_gpu(w, steps, warmup, seed=0, variant=()):
         seg = bps.Segments(t(sg["ids_q"]), t(sg.get("pos_q")), t(sg.get("ids_kv")), t(sg.get("pos_kv")))
     fwd = bps.FwdPlan(dev["q"], dev["k"], dev["v"], causal=w.causal, segments=seg, **fwd_var)
     bwd = bps.BwdPlan(dev["q"], dev["k"], dev["v"], fwd.o, fwd.lse, dev["do"], causal=w.causal, segments=seg,
-                      **bwd_var)
+                      flags=flags, **bwd_var)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -367,6 +367,9 @@ def main():
                     help="comma list of attention variants to run through attn_fwd_ex / attn_bwd_ex: bias "
                          "(per-row [B, Hq, Sq, Skv] bias with its gradient), softcap (soft-capping at "
                          f"{VARIANT_SOFTCAP:g}), sink (sink logits with their gradient), max_logit")
+    ap.add_argument("--fused-bwd", action="store_true",
+                    help="time the single-pass backward (ATTN_FUSED_BWD): the dK/dV kernel also writes dQ "
+                         "partials, the dQ phase sums them in key-tile order")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -404,7 +407,11 @@ def main():
     unknown = set(variant) - {"bias", "softcap", "sink", "max_logit"}
     if unknown:
         raise SystemExit(f"unknown --variant entries {sorted(unknown)}")
-    case, wall, avg, med, route = run_gpu(w, args.steps, args.warmup, variant=variant)
+    if args.fused_bwd and set(variant) - {"sink", "max_logit"}:
+        raise SystemExit("--fused-bwd takes no bias or soft cap")
+    import bwd_packed_segments_amd as bps
+    case, wall, avg, med, route = run_gpu(w, args.steps, args.warmup, variant=variant,
+                                          flags=bps.ATTN_FUSED_BWD if args.fused_bwd else 0)
     n = allowed_pairs(w, case["segments"])
     F = flops(w, n)
     f_step = F["fwd"] + F["bwd"]
@@ -414,6 +421,10 @@ def main():
 
     kernels = {"attn_fwd": (avg["fwd"], F["k_fwd"]), "attn_bwd_dkdv": (avg["dkdv"], F["k_dkdv"]),
                "attn_bwd_dq": (avg["dq"], F["k_dq"])}
+    if args.fused_bwd:
+        # the dK/dV phase runs all five backward products; the dQ phase only
+        # sums partials (bound by HBM, reported as its time in phase_ms)
+        kernels = {"attn_fwd": (avg["fwd"], F["k_fwd"]), "attn_bwd_fused": (avg["dkdv"], F["bwd"])}
     dom = max(kernels, key=lambda k: kernels[k][0])
     ms_dom, f_dom = kernels[dom]
     achieved = f_dom / (ms_dom * 1e-3) / 1e12
@@ -465,6 +476,10 @@ def main():
         out["config"]["variants"] = {"list": list(variant), "softcap": VARIANT_SOFTCAP if "softcap" in variant else 0,
                                      "bias": "[B, Hq, Sq, Skv] per batch row, N(0,1)" if "bias" in variant else None}
         args.no_cpu_baseline = True      # the baseline line is the plain workload's
+    if args.fused_bwd:
+        out["metric"] = out["metric"] + " (single-pass backward)"
+        out["config"]["backward"] = "single pass: dK/dV kernel with dQ partials, then a key-tile-ordered dQ sum"
+        args.no_cpu_baseline = True
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, case, f_step / w.Hq, args.cpu_seconds)
         cb.pop("seconds", None)

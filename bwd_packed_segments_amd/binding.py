@@ -19,6 +19,7 @@ ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_DEVICE = r
 ATTN_BF16, ATTN_FP32 = 0, 1
 ATTN_FORCE_GENERAL = 1 << 0
 ATTN_REVERSE_SCHEDULE = 1 << 1
+ATTN_FUSED_BWD = 1 << 2
 ROUTE_NAMES = {0: "dense", 1: "fast", 2: "general"}
 
 STATUS_NAMES = {

@@ -40,6 +40,8 @@ struct Plan {
   size_t off_route = 0, off_run_q = 0, off_pos_q = 0, off_sum_q = 0;
   size_t off_run_kv = 0, off_pos_kv = 0, off_sum_kv = 0;
   size_t off_delta = 0, off_lse2 = 0;
+  bool fused = false;           // ATTN_FUSED_BWD: dQ partials in the workspace
+  size_t off_dqp = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
 };
 
@@ -68,8 +70,12 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
     return fail(ATTN_E_UNSUPPORTED, "head dims (Dqk=%d, Dv=%d) not built for dtype %d", d->Dqk, d->Dv, d->dtype);
   if (d->causal != 0 && d->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
   if (!std::isfinite(d->scale) || d->scale < 0.f) return fail(ATTN_E_INVALID, "scale must be finite and >= 0");
-  if (d->flags & ~static_cast<uint32_t>(ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE))
+  if (d->flags & ~static_cast<uint32_t>(ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE | ATTN_FUSED_BWD))
     return fail(ATTN_E_INVALID, "unknown flag bits 0x%x", d->flags);
+  p->fused = (d->flags & ATTN_FUSED_BWD) != 0;
+  if (p->fused && (d->dtype != ATTN_BF16 || d->Dqk > 128 || d->Dv > 128))
+    return fail(ATTN_E_UNSUPPORTED, "the fused backward is built for bf16 with Dqk, Dv <= 128 (dtype %d, Dqk=%d, Dv=%d)",
+                d->dtype, d->Dqk, d->Dv);
   const long long rows = (long long)d->B * d->Hq * (long long)(d->Sq > d->Skv ? d->Sq : d->Skv);
   if (rows > (1LL << 31) - 1) return fail(ATTN_E_UNSUPPORTED, "B*H*S exceeds 2^31");
   const int vec = d->dtype == ATTN_BF16 ? 8 : 4;
@@ -120,6 +126,13 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
   const size_t nrow = (size_t)d->B * d->Hq * d->Sq;
   p->off_delta = off; off = align_up(off + nrow * sizeof(float));
   p->off_lse2 = off; off = align_up(off + nrow * sizeof(float));
+  if (p->fused) {
+    // One fp32 partial of 32 queries x Dqk per (batch row, query head, key
+    // tile of 128, query block of 32), query blocks padded to whole 64-row tiles.
+    const size_t n_kt = ((size_t)d->Skv + 127) / 128, nqb = 2 * (((size_t)d->Sq + 63) / 64);
+    p->off_dqp = off;
+    off = align_up(off + (size_t)d->B * d->Hq * n_kt * nqb * 32 * d->Dqk * sizeof(float));
+  }
   p->ws_bwd = off;
   return ATTN_OK;
 }
@@ -312,6 +325,7 @@ attn_status make_ring_plan(const attn_desc* d, const attn_segments* seg, int cp,
   attn_status st = make_plan(d, seg, &p);
   if (st != ATTN_OK) return st;
   if (cp < 1) return fail(ATTN_E_INVALID, "cp must be at least 1 (got %d)", cp);
+  if (p.fused) return fail(ATTN_E_UNSUPPORTED, "the ring emulation does not take ATTN_FUSED_BWD");
   if (d->Sq % cp || d->Skv % cp)
     return fail(ATTN_E_INVALID, "Sq (%d) and Skv (%d) must be multiples of cp (%d)", d->Sq, d->Skv, cp);
   rp->cp = cp;
@@ -418,6 +432,8 @@ attn_status make_var_plan(const attn_desc* d, const Plan& p, const attn_variant*
   if (!var) return ATTN_OK;
   if (!std::isfinite(var->softcap) || var->softcap < 0.f)
     return fail(ATTN_E_INVALID, "softcap must be finite and >= 0");
+  if (p.fused && (var->bias || var->softcap > 0.f))
+    return fail(ATTN_E_UNSUPPORTED, "the fused backward is not built for a bias or a soft cap");
   if (var->bias && var->bias_batch != 1 && var->bias_batch != d->B)
     return fail(ATTN_E_INVALID, "bias_batch must be 1 or B (%d), got %d", d->B, var->bias_batch);
   if (var->dbias && !var->bias) return fail(ATTN_E_INVALID, "dbias requested without a bias");
@@ -556,6 +572,7 @@ attn_status bwd_impl(int32_t phases, const attn_desc* d, const attn_segments* se
     a.sq = strides_of(d->q); a.sk = strides_of(d->k); a.sv = strides_of(d->v); a.so = strides_of(d->o);
     a.delta = reinterpret_cast<float*>(ws + p.off_delta);
     a.lse2 = reinterpret_cast<float*>(ws + p.off_lse2);
+    a.dqp = p.fused ? reinterpret_cast<float*>(ws + p.off_dqp) : nullptr;
     a.var = var_view(d, var, vp, ws, true);
     const bool prep = (phases & ATTN_BWD_PREPARE) != 0;
     const size_t esize = d->dtype == ATTN_BF16 ? 2 : 4;

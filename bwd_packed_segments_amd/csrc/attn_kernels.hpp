@@ -1125,7 +1125,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
 // matrix work, and each role fits half the register file.  The query tiles
 // are walked and classified exactly as in the kernel above, and every dK/dV
 // element is still written once, at the end, by its consumer wave.
-template <typename T, int DQK, int DV>
+//
+// DQP (the fused backward, for bf16 with Dqk <= 128): the producers also
+// store dS of each phase transposed, as a [128 keys x 32 queries] bf16 tile,
+// and each consumer wave then forms one 32-column block of the phase's dQ
+// partial, dS (32 x 128) times K (128 keys x 32 columns, held in registers),
+// and writes it to the dqp workspace.  No dQ value depends on the order in
+// which workgroups run: each partial is written by one wave, and the dQ
+// phase adds them up in ascending key-tile order.
+template <typename T, int DQK, int DV, bool DQP = false>
 struct DkvWsCfg {
   static constexpr int BN = 128;   // keys per workgroup: 4 key blocks of 32
   static constexpr int BM = 64;    // queries per step: 2 phases of 32
@@ -1135,19 +1143,24 @@ struct DkvWsCfg {
   static constexpr int SIDE_BYTES = BM * 4 * 4;
   static constexpr int STAGE_BYTES = Q_BYTES + DO_BYTES + SIDE_BYTES;
   static constexpr int XSLOT_BYTES = 4 * 4 * 64 * 16;   // 4 key blocks x (P, P, dS, dS) x 64 lanes x 16 B
-  static constexpr int LDS_BYTES = 3 * STAGE_BYTES + 2 * XSLOT_BYTES;
-  static constexpr bool ENABLED = sizeof(T) == 2 && DQK <= 192 && DV <= 128 && LDS_BYTES <= 160 * 1024;
+  static constexpr int DST_BYTES = DQP ? BN * 32 * (int)sizeof(T) : 0;   // dS^T tile of one phase
+  static constexpr int LDS_BYTES = 3 * STAGE_BYTES + 2 * XSLOT_BYTES + 2 * DST_BYTES;
+  static constexpr bool ENABLED = sizeof(T) == 2 && DQK <= 192 && DV <= 128 && LDS_BYTES <= 160 * 1024 &&
+                                  (!DQP || DQK <= 128);
+  static constexpr int PART = 32 * DQK;   // floats of one dQ partial (32 queries x Dqk)
 };
 
-template <typename T, int DQK, int DV, bool VAR>
+template <typename T, int DQK, int DV, bool VAR, bool DQP = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     attn_bwd_dkdv_ws_kernel(BwdArgs a) {
-  using C = DkvWsCfg<T, DQK, DV>;
+  using C = DkvWsCfg<T, DQK, DV, DQP>;
+  static_assert(!DQP || (!VAR && C::ENABLED), "the fused backward has no variant kernels");
   using E = Elem<T>;
   using F8 = typename E::F8;
   constexpr int BM = C::BM, BN = C::BN;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   char* xch = smem + 3 * C::STAGE_BYTES;
+  char* dsx = xch + 2 * C::XSLOT_BYTES;   // DQP: dS^T tiles of the two exchange slots
 
   const AttnShape& s = a.s;
   const bool causal = s.causal != 0;
@@ -1270,6 +1283,24 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
       vf[t] = kj < s.Skv ? E::load8(vp + kj * a.sv.t + 16 * t + 8 * hf) : E::zero8();
     if (general) km = kv_meta(route, a.seg, b, s.Skv, kj);
   }
+  // DQP: consumer wave kb's B operands of dQ = dS K, column block kb: for
+  // keys k0 + 16 t + cmap(hf, e), column 32 kb + n (the key order of the
+  // transposed dS^T reads).
+  constexpr int NKT = DQP ? BN / 16 : 1;
+  F8 kq[NKT];
+  const bool dq_wave = DQP && !producer && kb < DQK / 32;
+  if constexpr (DQP) {
+    if (dq_wave) {
+      const T* kp = static_cast<const T*>(a.k) + b * a.sk.b + hkv * a.sk.h + 32 * kb + n;
+#pragma unroll
+      for (int t = 0; t < NKT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = k0 + 16 * t + 8 * (e >> 2) + 4 * hf + (e & 3);
+          kq[t][e] = key < s.Skv ? kp[(int64_t)key * a.sk.t] : T(0.f);
+        }
+    }
+  }
 
   // Producer phase: S, dP for queries qb*32.. of step x, then P and dS (bf16)
   // into exchange slot `slot`.
@@ -1328,10 +1359,18 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
       *xfrag(slot, s2) = E::cvt8(slots8(sa, s2));
       *xfrag(slot, 2 + s2) = E::cvt8(slots8(pa, s2));
     }
+    if constexpr (DQP) {
+      // dS^T[key kb * 32 + n][query rmap(hf, r)]: four runs of 4 queries.
+      T* dst = reinterpret_cast<T*>(dsx + slot * C::DST_BYTES);
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+        *reinterpret_cast<typename E::P4*>(dst + TileFmt<T, 32>::off(kb * 32 + n, 8 * grp + 4 * hf)) =
+            E::cvt4(f32x4{pa[4 * grp], pa[4 * grp + 1], pa[4 * grp + 2], pa[4 * grp + 3]});
+    }
   };
   // Consumer phase: dV^T += dO^T P, dK^T += Q^T dS for queries qb*32.. of
   // the stage (dO^T and Q^T by transpose reads).
-  auto consume = [&](const char* st, int qb, int slot) {
+  auto consume = [&](const char* st, int x, int qb, int slot) {
     const T* Qs = reinterpret_cast<const T*>(st);
     const T* dOs = Qs + BM * DQK;
     F8 pf[2], dsf[2];
@@ -1348,6 +1387,23 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int d = 0; d < DQK / 32; ++d)
         dka[d] = mma(frag_tr<T, DQK>(Qs, d * 32, qb * 32 + 16 * s2, lane), dsf[s2], dka[d]);
+    }
+    if constexpr (DQP) {
+      if (dq_wave) {
+        // Partial of queries tile_of(x) * BM + qb * 32 .. + 31, columns
+        // 32 kb .. + 31, over this workgroup's keys in ascending order.
+        const T* dst = reinterpret_cast<const T*>(dsx + slot * C::DST_BYTES);
+        f32x16 qacc = f32x16{};
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) qacc = mma(frag_tr<T, 32>(dst, 0, 16 * t, lane), kq[t], qacc);
+        const int h = hkv * g + x % g;
+        const int nqb = 2 * ((s.Sq + BM - 1) / BM);
+        const size_t part = (((size_t)b * s.Hq + h) * n_kt + krank) * nqb + tile_of(x) * 2 + qb;
+        f32x4* out = reinterpret_cast<f32x4*>(a.dqp + part * C::PART + (size_t)(kb * 64 + lane) * 16);
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp)
+          out[grp] = f32x4{qacc[4 * grp], qacc[4 * grp + 1], qacc[4 * grp + 2], qacc[4 * grp + 3]};
+      }
     }
   };
 
@@ -1418,7 +1474,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     __syncthreads();   // phase 0: the producers' first phase
     int slot = 0;
     while (t.x < nsteps) {
-      consume(smem + t.buf * C::STAGE_BYTES, t.qb, slot);
+      consume(smem + t.buf * C::STAGE_BYTES, t.x, t.qb, slot);
       __syncthreads();
       slot ^= 1;
       sched_next(t);
@@ -1442,6 +1498,62 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
         f32x4 v = f32x4{dva[d][4 * grp], dva[d][4 * grp + 1], dva[d][4 * grp + 2], dva[d][4 * grp + 3]};
         *reinterpret_cast<typename E::P4*>(dvp + d * 32 + 8 * grp + 4 * hf) = E::cvt4(v);
       }
+  }
+}
+
+// ------------------------------------------------------------ backward: dQ of the fused pass
+
+// dQ of one (batch row, query head, block of 32 queries) as the sum of the
+// partials the fused dK/dV kernel wrote, over key tiles in ascending order,
+// then times the softmax scale.  The key tiles that wrote a partial for the
+// block are found with the same range and tile classification as that
+// kernel's walk; a block no key tile visited gets dQ = 0.  One wave per
+// 32-column block; each lane owns the 16 values of its C-layout slot.
+template <typename T, int DQK>
+__global__ void __launch_bounds__(2 * DQK) attn_bwd_dq_reduce_kernel(BwdArgs a) {
+  using W = DkvWsCfg<T, DQK, 128, true>;
+  constexpr int BM = W::BM, BN = W::BN;
+  const AttnShape& s = a.s;
+  const int nqb = 2 * ((s.Sq + BM - 1) / BM);
+  const int n_kt = (s.Skv + BN - 1) / BN;
+  int L = blockIdx.x;
+  const int qblk = L % nqb;
+  L /= nqb;
+  const int h = L % s.Hq;
+  const int b = L / s.Hq;
+  const int qt = qblk >> 1;
+  const int j = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const bool causal = s.causal != 0;
+
+  const int route = s.has_meta ? a.seg.route[b] : kRouteDense;
+  TileSum qs{};
+  if (route != kRouteDense) qs = tile_sum(a.seg.sum_q + (size_t)b * a.seg.nch_q, a.seg.nch_q, qt * BM, BM);
+  const float* part = a.dqp + (((size_t)b * s.Hq + h) * n_kt * nqb + qblk) * W::PART + (size_t)(j * 64 + lane) * 16;
+  f32x16 acc = f32x16{};
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * BN;
+    TileSum ks{};
+    if (route != kRouteDense) ks = tile_sum(a.seg.sum_kv + (size_t)b * a.seg.nch_kv, a.seg.nch_kv, k0, BN);
+    int lo, hi;
+    q_range(route, causal, s.Sq, k0, BN, ks, lo, hi);
+    if (qt < lo / BM || qt >= (hi + BM - 1) / BM) continue;
+    if (classify_tile(route, causal, s.Skv, qt * BM, BM, k0, BN, qs, ks) == kTileSkip) continue;
+    const f32x4* p = reinterpret_cast<const f32x4*>(part + (size_t)kt * nqb * W::PART);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 v = p[grp];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[4 * grp + i] += v[i];
+    }
+  }
+  T* dq = static_cast<T*>(a.dq) + b * a.sq.b + h * a.sq.h + 32 * j + n;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = qblk * 32 + rmap(hf, r);
+    if (i < s.Sq) dq[(int64_t)i * a.sq.t] = T(acc[r] * s.scale);
   }
 }
 
@@ -1490,11 +1602,26 @@ hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The fused backward (a.dqp set) is built for bf16 with Dqk, Dv <= 128 and
+// no bias or soft cap; the host checks this before any launch.
+template <typename T, int DQK, int DV>
+constexpr bool kFusedBwd = sizeof(T) == 2 && DQK <= 128 && DV <= 128 &&
+                           DkvWsCfg<T, DQK, DV, true>::ENABLED;
+
 template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
   const int n_kt = (a.s.Skv + DkvCfg<T, DQK, DV>::BN - 1) / DkvCfg<T, DQK, DV>::BN;
   const long long nblocks = (long long)a.s.B * a.s.Hkv * n_kt;
   if (nblocks <= 0) return hipSuccess;
+  if (a.dqp != nullptr) {
+    if constexpr (!VAR && kFusedBwd<T, DQK, DV>) {
+      static_assert(DkvWsCfg<T, DQK, DV, true>::BN == DkvCfg<T, DQK, DV>::BN, "same key tiling");
+      hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, false, true>), dim3((unsigned)nblocks), dim3(512), 0,
+                         st, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if constexpr (DkvWsCfg<T, DQK, DV>::ENABLED) {
     static_assert(DkvWsCfg<T, DQK, DV>::BN == DkvCfg<T, DQK, DV>::BN, "same key tiling");
     hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(512), 0, st, a);
@@ -1506,6 +1633,15 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
 
 template <typename T, int DQK, int DV, bool VAR>
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
+  if (a.dqp != nullptr) {
+    if constexpr (!VAR && kFusedBwd<T, DQK, DV>) {
+      const long long nb = (long long)a.s.B * a.s.Hq * 2 * ((a.s.Sq + 63) / 64);
+      if (nb <= 0) return hipSuccess;
+      hipLaunchKernelGGL((attn_bwd_dq_reduce_kernel<T, DQK>), dim3((unsigned)nb), dim3(2 * DQK), 0, st, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   const int n_qt = (a.s.Sq + DqCfg<T, DQK, DV>::BM - 1) / DqCfg<T, DQK, DV>::BM;
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;

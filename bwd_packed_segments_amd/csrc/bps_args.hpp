@@ -67,6 +67,12 @@ struct BwdArgs {
   Strides sq, sk, sv, so;
   float* delta;      // [B, Hq, Sq] workspace: rowsum(dO * O)
   float* lse2;       // [B, Hq, Sq] workspace: LSE * log2(e), +inf for empty rows
+  // Fused backward (NULL: separate dK/dV and dQ kernels).  The dK/dV kernel
+  // also writes, per (batch row, query head, key tile of 128, query block
+  // of 32), the fp32 partial sum dS K over that key tile (unscaled) in MFMA
+  // C layout, [Dqk / 32 column blocks][64 lanes][16]; the dQ phase sums the
+  // partials of each query block over key tiles in ascending order.
+  float* dqp;        // [B, Hq, ceil(Skv / 128), 2 ceil(Sq / 64), 32 Dqk] workspace
   SegView seg;
   VarView var;
 };

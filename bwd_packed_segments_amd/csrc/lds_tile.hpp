@@ -47,6 +47,11 @@ struct TileFmt {
       return c ^ (4 * (r & 3) + ((r >> 2) & 3));
     } else if constexpr (NC == 8) {
       return c ^ (2 * (r & 3) + ((r >> 2) & 1));
+    } else if constexpr (NC == 4) {
+      // 64-byte rows (the fused backward's dS^T tile): transposed reads of 4
+      // consecutive rows cover 256 contiguous bytes whatever f is; f = bits
+      // 2-3 of the row halves the conflicts of column-wise 8-byte stores.
+      return c ^ ((r >> 2) & 3);
     } else {
       static_assert(NC == 24, "unsupported row width");
       const int f = 4 * (r & 3) + ((r >> 2) & 3);

@@ -90,9 +90,29 @@ typedef enum {
 /* attn_desc.flags */
 enum {
   ATTN_FORCE_GENERAL = 1u << 0,     /* never take the fast route (tests, ring steps) */
-  ATTN_REVERSE_SCHEDULE = 1u << 1   /* visit workgroup tiles in reverse order (tests:
+  ATTN_REVERSE_SCHEDULE = 1u << 1,  /* visit workgroup tiles in reverse order (tests:
                                        results must not depend on schedule) */
+  ATTN_FUSED_BWD = 1u << 2          /* backward: single-pass form (see below) */
 };
+
+/* ATTN_FUSED_BWD: the single-pass backward of the maxdiffusion page on custom
+ * splash and ring attention (Key Features: one kernel over key blocks, query
+ * blocks inside, computes dQ, dK and dV, and dQ is reduced across key
+ * blocks).  The dK/dV kernel, which already forms dS for every allowed
+ * (query, key) tile, also multiplies it by K and writes one fp32 dQ partial
+ * per (batch row, query head, key tile of 128, query block of 32) into the
+ * workspace; the DQ phase then adds each block's partials over key tiles in
+ * ascending order and scales them.  So S and dP are formed once instead of
+ * twice (five products instead of seven), and, as that page's code review
+ * demands of any dQ reduction, no result depends on the order workgroups
+ * run in: outputs are bitwise reproducible and dK, dV are bitwise those of
+ * the two-kernel backward.  dQ equals the two-kernel dQ up to fp32
+ * summation order (a sum of per-tile partials instead of one running sum).
+ * Costs: workspace of B * Hq * ceil(Skv / 128) * 64 ceil(Sq / 64) * Dqk * 4
+ * bytes more (17.2 GB at B = 1, Hq = 64, S = 8192, Dqk = 128), written and
+ * read once per call.  Built for bf16 with Dqk, Dv <= 128 and no bias or soft
+ * cap (ATTN_E_UNSUPPORTED otherwise); the ring emulation does not take it.
+ * attn_fwd ignores the flag. */
 
 /* Route reported through route_out. */
 enum {
@@ -115,7 +135,8 @@ typedef struct {
   int32_t dtype;                    /* attn_dtype */
   int32_t causal;                   /* 0 or 1 */
   float scale;                      /* softmax scale; 0 selects 1/sqrt(Dqk) */
-  uint32_t flags;                   /* ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE */
+  uint32_t flags;                   /* ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE |
+                                       ATTN_FUSED_BWD */
   attn_strides q, k, v, o;          /* layouts of Q, K, V, O (and dQ, dK, dV, dO) */
 } attn_desc;
 
@@ -158,7 +179,8 @@ attn_status attn_bwd(const attn_desc* desc, const attn_segments* seg,
  * that DKDV and DQ then read, so it must complete first on the stream (or be
  * ordered before them with events) and the workspace must not change in
  * between; DKDV and DQ are independent of each other and may run on two
- * streams at once.  Arguments a phase does not use may be NULL (PREPARE uses
+ * streams at once, except under ATTN_FUSED_BWD, where DQ sums the partials
+ * DKDV writes and must be ordered after it.  Arguments a phase does not use may be NULL (PREPARE uses
  * o, lse, dout; DKDV uses q, k, v, dout, dk, dv; DQ uses q, k, v, dout, dq).
  * Same descriptor, metadata and workspace size rules as attn_bwd. */
 enum {

@@ -230,3 +230,30 @@ def test_variant_workspace_sizes():
     f, b = B.ex_workspace_sizes(d, _var(bias=ptr, bias_batch=2, dbias=ptr))
     assert b == plain[1]                                              # written in place
     assert B.ex_workspace_sizes(d, _var(softcap=-1.0)) == (0, 0)
+
+
+def test_fused_bwd_validation_and_workspace():
+    F = B.ATTN_FUSED_BWD
+    d = good(B=2, Sq=300, Skv=260, Hq=4, Hkv=2, Dqk=128, Dv=64, causal=False)
+    plain = B.bwd_workspace_size(d)
+    fused = B.bwd_workspace_size(good(B=2, Sq=300, Skv=260, Hq=4, Hkv=2, Dqk=128, Dv=64, causal=False, flags=F))
+    # one fp32 partial of 32 queries x Dqk per (row, head, key tile of 128, query block of 32),
+    # query blocks padded to whole 64-row tiles: 3 key tiles, 10 query blocks
+    assert fused >= plain + 2 * 4 * 3 * 10 * 32 * 128 * 4
+    assert fused < plain + 2 * 4 * 3 * 10 * 32 * 128 * 4 + 512
+    assert B.fwd_workspace_size(good(flags=F)) == B.fwd_workspace_size(good())   # the forward ignores it
+    for kw, word in ((dict(dtype=B.ATTN_FP32, Dqk=64, Dv=64), "bf16"), (dict(Dqk=192), "Dqk")):
+        st, text = B.validate_bwd(good(flags=F, **kw))
+        assert st == B.ATTN_E_UNSUPPORTED and word in text, (st, text)
+        assert B.bwd_workspace_size(good(flags=F, **kw)) == 0
+    # no bias or soft cap in the fused form; a sink (read through the LSE) is fine
+    ptr = 1 << 12
+    st, text = B.validate_ex(good(flags=F), _var(softcap=2.0), bwd=True)
+    assert st == B.ATTN_E_UNSUPPORTED and "fused" in text
+    st, text = B.validate_ex(good(flags=F), _var(bias=ptr, bias_batch=2), bwd=True)
+    assert st == B.ATTN_E_UNSUPPORTED and "fused" in text
+    assert B.ex_workspace_sizes(good(flags=F), _var(sink=ptr))[1] == B.bwd_workspace_size(good(flags=F))
+    st, text = B.validate_ring_fwd(good(flags=F), None, 2)
+    assert st == B.ATTN_E_UNSUPPORTED and "ring" in text
+    st, text = B.validate_bwd(good(flags=1 << 3))
+    assert st == B.ATTN_E_INVALID and "flag" in text
