@@ -11,7 +11,7 @@ Notation (shared with the tests):
   segments: dict with "ids_q", "pos_q", "ids_kv", "pos_kv", each int32
   [B, S] or None.  ids 0 marks padding.
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open:
   * id 0 is padding: a query with id 0 attends nothing, a key with id 0 is
     attended by nothing.
   * with segment metadata, causal compares positions, pos_kv[j] <= pos_q[i],

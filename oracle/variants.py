@@ -14,7 +14,7 @@ beside the Q/K/V gradients (Diagram; Changes 5 and 6 reduce dBias across
 data-parallel axes); the TransformerEngine page "[JAX] Make all jax
 attention calls use non-packed common calls" links a change adding sink
 attention.  None of them writes the equations, so the readings below are the
-plainest ones in common use; each is listed in the design doc:
+plainest ones in common use:
 
   * logits:   X_ij = scale * <q_i, k_j> + bias[b', h, i, j]
               (bias [Bb, Hq, Sq, Skv], Bb = 1 shared by every batch row or
