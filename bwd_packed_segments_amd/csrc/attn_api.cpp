@@ -3,6 +3,7 @@
 // argument error is reported (and nothing launched) even without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -42,6 +43,8 @@ struct Plan {
   size_t off_delta = 0, off_lse2 = 0;
   bool fused = false;           // ATTN_FUSED_BWD: dQ partials in the workspace
   size_t off_dqp = 0;
+  int kv_split = 1;             // workgroups per key tile in dK/dV (partials when > 1)
+  size_t off_dkvp = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
 };
 
@@ -132,6 +135,16 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
     const size_t n_kt = ((size_t)d->Skv + 127) / 128, nqb = 2 * (((size_t)d->Sq + 63) / 64);
     p->off_dqp = off;
     off = align_up(off + (size_t)d->B * d->Hq * n_kt * nqb * 32 * d->Dqk * sizeof(float));
+  }
+  // bf16 dK/dV with fewer than two workgroups per CU (256 CUs): split each
+  // key tile's walk over query tiles between up to 4 workgroups, so the
+  // longest walk no longer sets the time alone; the parts are fp32 partials
+  // summed in split order by a second kernel.
+  const size_t n_kt = ((size_t)d->Skv + 127) / 128, nkvb = (size_t)d->B * d->Hkv * n_kt;
+  if (d->dtype == ATTN_BF16 && nkvb > 0 && nkvb < 512) {
+    p->kv_split = (int)std::min<size_t>(4, (512 + nkvb - 1) / nkvb);
+    p->off_dkvp = off;
+    off = align_up(off + nkvb * p->kv_split * 128 * (size_t)(d->Dqk + d->Dv) * sizeof(float));
   }
   p->ws_bwd = off;
   return ATTN_OK;
@@ -573,6 +586,8 @@ attn_status bwd_impl(int32_t phases, const attn_desc* d, const attn_segments* se
     a.delta = reinterpret_cast<float*>(ws + p.off_delta);
     a.lse2 = reinterpret_cast<float*>(ws + p.off_lse2);
     a.dqp = p.fused ? reinterpret_cast<float*>(ws + p.off_dqp) : nullptr;
+    a.kv_split = p.kv_split;
+    a.dkvp = p.kv_split > 1 ? reinterpret_cast<float*>(ws + p.off_dkvp) : nullptr;
     a.var = var_view(d, var, vp, ws, true);
     const bool prep = (phases & ATTN_BWD_PREPARE) != 0;
     const size_t esize = d->dtype == ATTN_BF16 ? 2 : 4;

@@ -1178,7 +1178,7 @@ struct DkvWsCfg {
   static constexpr int PART = 32 * DQK;   // floats of one dQ partial (32 queries x Dqk)
 };
 
-template <typename T, int DQK, int DV, bool VAR, bool DQP = false>
+template <typename T, int DQK, int DV, bool VAR, bool DQP = false, bool SPLIT = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     attn_bwd_dkdv_ws_kernel(BwdArgs a) {
   using C = DkvWsCfg<T, DQK, DV, DQP>;
@@ -1194,8 +1194,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
   const bool causal = s.causal != 0;
   const int n_kt = (s.Skv + BN - 1) / BN;
   const int g = s.Hq / s.Hkv;
-  const int nblocks = s.B * s.Hkv * n_kt;
+  const int nsplit = SPLIT ? a.kv_split : 1;   // a separate instance, so the unsplit code stays lean
+  const int nblocks = s.B * s.Hkv * n_kt * nsplit;
   int L = logical_block(nblocks, s.reverse);
+  const int split = L % nsplit;
+  L /= nsplit;
   const int krank = L % n_kt;
   L /= n_kt;
   const int hkv = L % s.Hkv;
@@ -1224,7 +1227,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
   q_range(route, causal, s.Sq, k0, BN, ks, lo, hi);
   const int t_hi = (hi + BM - 1) / BM;
   const int ntiles = t_hi - lo / BM;
-  const int nsteps = g * ntiles;
+  // This workgroup's part of the walk: tiles [u0, u1) in walk order, steps
+  // [x0, nsteps) (all of it unless the walk is split).
+  const int u0 = split * ntiles / nsplit, u1 = (split + 1) * ntiles / nsplit;
+  const int x0 = g * u0;
+  const int nsteps = g * u1;
   auto tile_of = [&](int x) { return t_hi - 1 - x / g; };
   auto classify = [&](int qt) -> int {
     TileSum qs{};
@@ -1447,7 +1454,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
   };
   auto sched_init = [&]() {
     Sched t;
-    t.x = next_step(0, t.cls);
+    t.x = next_step(x0, t.cls);
     t.nx = t.x < nsteps ? next_step(t.x + 1, t.ncls) : nsteps;
     t.buf = 0;
     t.qb = 0;
@@ -1509,7 +1516,26 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     }
   }
 
-  if (!producer && kj < s.Skv) {
+  if (SPLIT) {
+    // fp32 partials, float4-index-major so that every store instruction
+    // writes 1 KB of contiguous memory.
+    if (!producer) {
+      constexpr int NF4 = 4 * (DQK / 32 + DV / 32);
+      f32x4* out = reinterpret_cast<f32x4*>(a.dkvp) +
+                   (((((size_t)b * s.Hkv + hkv) * n_kt + krank) * nsplit + split) * 4 + kb) * NF4 * 64 + lane;
+      int i = 0;
+#pragma unroll
+      for (int d = 0; d < DQK / 32; ++d)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp, ++i)
+          out[i * 64] = f32x4{dka[d][4 * grp], dka[d][4 * grp + 1], dka[d][4 * grp + 2], dka[d][4 * grp + 3]};
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp, ++i)
+          out[i * 64] = f32x4{dva[d][4 * grp], dva[d][4 * grp + 1], dva[d][4 * grp + 2], dva[d][4 * grp + 3]};
+    }
+  } else if (!producer && kj < s.Skv) {
     T* dkp = static_cast<T*>(a.dk) + b * a.sk.b + kj * a.sk.t + hkv * a.sk.h;
     T* dvp = static_cast<T*>(a.dv) + b * a.sv.b + kj * a.sv.t + hkv * a.sv.h;
 #pragma unroll
@@ -1526,6 +1552,47 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
         f32x4 v = f32x4{dva[d][4 * grp], dva[d][4 * grp + 1], dva[d][4 * grp + 2], dva[d][4 * grp + 3]};
         *reinterpret_cast<typename E::P4*>(dvp + d * 32 + 8 * grp + 4 * hf) = E::cvt4(v);
       }
+  }
+}
+
+// ------------------------------------------------------------ backward: split dK/dV walks
+
+// dK (times the softmax scale) and dV of one key tile from the kv_split
+// partials of its split walk, added in split order.  One wave per 32-key
+// block, each lane the C-layout values the consumer wave held.
+template <typename T, int DQK, int DV>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_reduce_kernel(BwdArgs a) {
+  using E = Elem<T>;
+  constexpr int BN = DkvWsCfg<T, DQK, DV>::BN;
+  constexpr int NF4 = 4 * (DQK / 32 + DV / 32);
+  const AttnShape& s = a.s;
+  const int nsplit = a.kv_split;
+  const int n_kt = (s.Skv + BN - 1) / BN;
+  int L = blockIdx.x;
+  const int krank = L % n_kt;
+  L /= n_kt;
+  const int hkv = L % s.Hkv;
+  const int b = L / s.Hkv;
+  const int kb = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const int kj = krank * BN + kb * 32 + n;
+  const size_t stride = (size_t)4 * NF4 * 64;   // between the partials of consecutive splits
+  const f32x4* part = reinterpret_cast<const f32x4*>(a.dkvp) +
+                      (((size_t)b * s.Hkv + hkv) * n_kt + krank) * nsplit * stride + (size_t)kb * NF4 * 64 + lane;
+  if (kj >= s.Skv) return;
+  T* dkp = static_cast<T*>(a.dk) + b * a.sk.b + kj * a.sk.t + hkv * a.sk.h;
+  T* dvp = static_cast<T*>(a.dv) + b * a.sv.b + kj * a.sv.t + hkv * a.sv.h;
+#pragma unroll 4
+  for (int i = 0; i < NF4; ++i) {
+    f32x4 v = part[i * 64];
+    for (int sp = 1; sp < nsplit; ++sp) v += part[sp * stride + i * 64];
+    const int d = (i >> 2) % (DQK / 32), grp = i & 3;
+    if (i < 4 * (DQK / 32))
+      *reinterpret_cast<typename E::P4*>(dkp + d * 32 + 8 * grp + 4 * hf) = E::cvt4(v * s.scale);
+    else
+      *reinterpret_cast<typename E::P4*>(dvp + ((i >> 2) - DQK / 32) * 32 + 8 * grp + 4 * hf) = E::cvt4(v);
   }
 }
 
@@ -1641,20 +1708,35 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
   const int n_kt = (a.s.Skv + DkvCfg<T, DQK, DV>::BN - 1) / DkvCfg<T, DQK, DV>::BN;
   const long long nblocks = (long long)a.s.B * a.s.Hkv * n_kt;
   if (nblocks <= 0) return hipSuccess;
+  if (a.kv_split < 1 || (a.kv_split > 1 && (!DkvWsCfg<T, DQK, DV>::ENABLED || a.dkvp == nullptr)))
+    return hipErrorInvalidValue;
+  const unsigned nws = (unsigned)(nblocks * a.kv_split);
+  const bool split = a.kv_split > 1;
   if (a.dqp != nullptr) {
     if constexpr (!VAR && kFusedBwd<T, DQK, DV>) {
       static_assert(DkvWsCfg<T, DQK, DV, true>::BN == DkvCfg<T, DQK, DV>::BN, "same key tiling");
-      hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, false, true>), dim3((unsigned)nblocks), dim3(512), 0,
-                         st, a);
-      return hipGetLastError();
+      if (split)
+        hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, false, true, true>), dim3(nws), dim3(512), 0, st, a);
+      else
+        hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, false, true>), dim3(nws), dim3(512), 0, st, a);
+    } else {
+      return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
-  }
-  if constexpr (DkvWsCfg<T, DQK, DV>::ENABLED) {
+  } else if constexpr (DkvWsCfg<T, DQK, DV>::ENABLED) {
     static_assert(DkvWsCfg<T, DQK, DV>::BN == DkvCfg<T, DQK, DV>::BN, "same key tiling");
-    hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(512), 0, st, a);
+    if (split)
+      hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, VAR, false, true>), dim3(nws), dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, VAR>), dim3(nws), dim3(512), 0, st, a);
   } else {
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DQK, DV, VAR>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  }
+  if constexpr (DkvWsCfg<T, DQK, DV>::ENABLED) {
+    if (a.kv_split > 1) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_bwd_dkdv_reduce_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+    }
   }
   return hipGetLastError();
 }

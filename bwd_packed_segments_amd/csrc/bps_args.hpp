@@ -75,6 +75,13 @@ struct BwdArgs {
   float* dqp;        // [B, Hq, ceil(Skv / 128), 2 ceil(Sq / 64), 32 Dqk] workspace
   SegView seg;
   VarView var;
+  // Split dK/dV walks (bf16 kernels): with kv_split > 1, kv_split workgroups
+  // share each key tile's walk over query tiles (contiguous, nearly equal
+  // parts) and write fp32 partials of dK (unscaled) and dV, which a second
+  // kernel adds up in split order.  Small grids (fewer than two workgroups
+  // per CU) otherwise leave the time to the longest walk alone.
+  int kv_split;      // 1: one workgroup per key tile, dK/dV written directly
+  float* dkvp;       // [B, Hkv, ceil(Skv / 128), kv_split, 128 (Dqk + Dv)] workspace
 };
 
 struct SegMetaArgs {
