@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "bps_args.hpp"
@@ -137,12 +138,19 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
     off = align_up(off + (size_t)d->B * d->Hq * n_kt * nqb * 32 * d->Dqk * sizeof(float));
   }
   // bf16 dK/dV with fewer than two workgroups per CU (256 CUs): split each
-  // key tile's walk over query tiles between up to 4 workgroups, so the
-  // longest walk no longer sets the time alone; the parts are fp32 partials
-  // summed in split order by a second kernel.
+  // key tile's walk over query tiles between 2 to 4 workgroups, about three
+  // per CU in all, so the longest walk no longer sets the time alone; the
+  // parts are fp32 partials summed in split order by a second kernel.
+  // (Cross 4K, 256 key tiles: 0.92 / 0.73 / 0.62 / 0.73 ms for 1 / 2 / 3 / 4
+  // parts.)
   const size_t n_kt = ((size_t)d->Skv + 127) / 128, nkvb = (size_t)d->B * d->Hkv * n_kt;
-  if (d->dtype == ATTN_BF16 && nkvb > 0 && nkvb < 512) {
-    p->kv_split = (int)std::min<size_t>(4, (512 + nkvb - 1) / nkvb);
+  int split = (nkvb > 0 && nkvb < 512) ? (int)std::min<size_t>(4, std::max<size_t>(2, (768 + nkvb / 2) / nkvb)) : 1;
+  if (const char* e = getenv("BPS_KV_SPLIT")) {   // comparison switch: force 1-4 parts
+    const int f = atoi(e);
+    if (f >= 1 && f <= 4) split = f;
+  }
+  if (d->dtype == ATTN_BF16 && nkvb > 0 && split > 1) {
+    p->kv_split = split;
     p->off_dkvp = off;
     off = align_up(off + nkvb * p->kv_split * 128 * (size_t)(d->Dqk + d->Dv) * sizeof(float));
   }

@@ -260,8 +260,9 @@ def test_fused_bwd_validation_and_workspace():
 
 
 def test_split_dkdv_workspace():
-    """bf16 dK/dV grids of fewer than 512 workgroups split each key tile's
-    walk (up to 4 ways) into fp32 partials held in the workspace."""
+    """bf16 dK/dV grids of fewer than 512 key tiles split each key tile's
+    walk (2 to 4 ways, about 768 parts in all) into fp32 partials held in
+    the workspace."""
     row = 2 * 4 * 300 * 4                                   # one fp32 per (batch row, head, query)
     small = good(B=2, Sq=300, Skv=300, Hq=4, Hkv=2)         # 2 x 2 x 3 = 12 key tiles -> 4 parts
     assert B.bwd_workspace_size(small) >= 2 * row + 12 * 4 * 128 * 256 * 4
@@ -269,6 +270,9 @@ def test_split_dkdv_workspace():
     assert B.bwd_workspace_size(fp32) < 2 * row + 1024      # fp32 kernels never split
     big = good(B=1, Sq=8192, Skv=8192, Hq=64, Hkv=8)        # 8 x 64 = 512 key tiles: no split
     assert B.bwd_workspace_size(big) < 2 * 64 * 8192 * 4 + 1024
-    mid = good(B=1, Sq=4096, Skv=4096, Hq=32, Hkv=8, Dqk=192)   # 256 key tiles -> 2 parts
+    mid = good(B=1, Sq=4096, Skv=4096, Hq=32, Hkv=8, Dqk=192)   # 256 key tiles -> 3 parts
     extra = B.bwd_workspace_size(mid) - 2 * 32 * 4096 * 4
-    assert 256 * 2 * 128 * (192 + 128) * 4 <= extra < 256 * 2 * 128 * (192 + 128) * 4 + 1024
+    assert 256 * 3 * 128 * (192 + 128) * 4 <= extra < 256 * 3 * 128 * (192 + 128) * 4 + 1024
+    wide = good(B=1, Sq=4096, Skv=4096, Hq=48, Hkv=12, Dqk=128)  # 384 key tiles -> 2 parts
+    extra = B.bwd_workspace_size(wide) - 2 * 48 * 4096 * 4
+    assert 384 * 2 * 128 * 256 * 4 <= extra < 384 * 2 * 128 * 256 * 4 + 1024
