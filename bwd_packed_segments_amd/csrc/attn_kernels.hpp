@@ -1358,15 +1358,55 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
       bq = bias_queries<T>(bcol, ib, s.Sq, s.Skv, hf);
     }
     F8 qa[DQK / 16], da[DV / 16];
-#pragma unroll
-    for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
-#pragma unroll
-    for (int t = 0; t < DV / 16; ++t) da[t] = frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf);
     f32x16 sa = f32x16{}, pa = f32x16{};
+    bool expd = false;   // exponentials of S already taken with the dP products
+    if constexpr (!VAR && !DQP) {
+      // Every Q fragment of S is read before the first product, so the S
+      // chain runs back to back instead of waiting one LDS round trip per
+      // product; the dO fragments and LSE values are read between the S
+      // products, and the exponentials of S run between the dP products.
 #pragma unroll
-    for (int t = 0; t < DQK / 16; ++t) sa = mma(qa[t], kf[t], sa);
+      for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
+      __builtin_amdgcn_sched_group_barrier(0x100, DQK / 16, 0);
+      f32x4 l4[4];
 #pragma unroll
-    for (int t = 0; t < DV / 16; ++t) pa = mma(da[t], vf[t], pa);
+      for (int t = 0; t < DQK / 16; ++t) {
+        sa = mma(qa[t], kf[t], sa);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (t < DV / 16) {
+          da[t] = frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (t >= DQK / 16 - 4) {
+          const int grp = t - (DQK / 16 - 4);
+          l4[grp] = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+#pragma unroll
+      for (int t = DQK / 16; t < DV / 16; ++t) da[t] = frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf);
+#pragma unroll
+      for (int t = 0; t < DV / 16; ++t) {
+        pa = mma(da[t], vf[t], pa);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int grp = t * 4 / (DV / 16); grp < (t + 1) * 4 / (DV / 16); ++grp) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[grp][i]));
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+      }
+      expd = true;
+    } else {
+#pragma unroll
+      for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
+#pragma unroll
+      for (int t = 0; t < DV / 16; ++t) da[t] = frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf);
+#pragma unroll
+      for (int t = 0; t < DQK / 16; ++t) sa = mma(qa[t], kf[t], sa);
+#pragma unroll
+      for (int t = 0; t < DV / 16; ++t) pa = mma(da[t], vf[t], pa);
+    }
     if constexpr (VAR) {
       // Variant logits, masked to -inf, then P and dLoss/dx = P (dP - Delta)
       // dS/dx in one pass; dx also goes to the dbias target.
@@ -1375,11 +1415,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
       var_softgrad(sa, pa, lse2s + qb * 32, deltas + qb * 32, a.var, hf);
       if (a.var.dbias != nullptr && kj < s.Skv) var_store_dx<T>(pa, a.var, b * a.var.dbias_b + col, ib, s.Sq, s.Skv, hf);
     } else {
+      if (!expd) {
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
+        for (int grp = 0; grp < 4; ++grp) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[i]));
+          for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[i]));
+        }
       }
       if (part) mask_tile<false>(sa, 0.f, route, causal, s.Skv, kj, km, tile_of(x) * BM + qb * 32, hf, qma, qmb, qb * 32);
 #pragma unroll
