@@ -1359,12 +1359,21 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     }
     F8 qa[DQK / 16], da[DV / 16];
     f32x16 sa = f32x16{}, pa = f32x16{};
-    bool expd = false;   // exponentials of S already taken with the dP products
-    if constexpr (!VAR && !DQP) {
+    // Plain instance: exponentials of S taken with the dP products, and
+    // (Dqk <= 128) Delta read during them.
+    constexpr bool PRE = !VAR && !DQP;
+    constexpr bool PRE_DELTA = PRE && DQK <= 128;
+    f32x4 dl[4];
+    if constexpr (PRE) {
       // Every Q fragment of S is read before the first product, so the S
       // chain runs back to back instead of waiting one LDS round trip per
       // product; the dO fragments and LSE values are read between the S
-      // products, and the exponentials of S run between the dP products.
+      // products, the exponentials of S run between the dP products, and
+      // (Dqk <= 128) the Delta values are read with them: read after the
+      // products, they cost two LDS round trips at the end of every phase
+      // (same host: dK/dV 2.48-2.50 against 2.62-2.67 ms on the 8K causal
+      // GQA workload; with Dqk = 192 it was 5 % slower, so that keeps the
+      // late reads).
 #pragma unroll
       for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
       __builtin_amdgcn_sched_group_barrier(0x100, DQK / 16, 0);
@@ -1385,6 +1394,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
       }
 #pragma unroll
       for (int t = DQK / 16; t < DV / 16; ++t) da[t] = frag_row<T, DV>(dOs, qb * 32 + n, 16 * t + 8 * hf);
+      // The S and dP chains are scheduled apart, so that the Delta reads
+      // below cannot take the place of the Q fragment reads ahead of S.
+      if constexpr (PRE_DELTA) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < DV / 16; ++t) {
         pa = mma(da[t], vf[t], pa);
@@ -1394,9 +1406,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
           for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[grp][i]));
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          if constexpr (PRE_DELTA) {
+            dl[grp] = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
         }
       }
-      expd = true;
     } else {
 #pragma unroll
       for (int t = 0; t < DQK / 16; ++t) qa[t] = frag_row<T, DQK>(Qs, qb * 32 + n, 16 * t + 8 * hf);
@@ -1415,7 +1430,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
       var_softgrad(sa, pa, lse2s + qb * 32, deltas + qb * 32, a.var, hf);
       if (a.var.dbias != nullptr && kj < s.Skv) var_store_dx<T>(pa, a.var, b * a.var.dbias_b + col, ib, s.Sq, s.Skv, hf);
     } else {
-      if (!expd) {
+      if constexpr (!PRE) {
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qb * 32 + 8 * grp + 4 * hf);
@@ -1426,7 +1441,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
       if (part) mask_tile<false>(sa, 0.f, route, causal, s.Skv, kj, km, tile_of(x) * BM + qb * 32, hf, qma, qmb, qb * 32);
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
+        f32x4 d4;
+        if constexpr (PRE_DELTA) d4 = dl[grp];
+        else d4 = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
 #pragma unroll
         for (int i = 0; i < 4; ++i) pa[4 * grp + i] = sa[4 * grp + i] * (pa[4 * grp + i] - d4[i]);
       }
