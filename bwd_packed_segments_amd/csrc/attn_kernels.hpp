@@ -1401,15 +1401,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
       for (int t = 0; t < DV / 16; ++t) {
         pa = mma(da[t], vf[t], pa);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (PRE_DELTA) {
+          if (t < 4) {
+            dl[t] = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * t + 4 * hf);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
 #pragma unroll
         for (int grp = t * 4 / (DV / 16); grp < (t + 1) * 4 / (DV / 16); ++grp) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) sa[4 * grp + i] = fast_exp2(fmaf(sa[4 * grp + i], c2, -l4[grp][i]));
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-          if constexpr (PRE_DELTA) {
-            dl[grp] = *reinterpret_cast<const f32x4*>(deltas + qb * 32 + 8 * grp + 4 * hf);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
         }
       }
     } else {
