@@ -1727,7 +1727,23 @@ __global__ void __launch_bounds__(2 * DQK) attn_bwd_dq_reduce_kernel(BwdArgs a) 
   }
 }
 
+}  // namespace bps
+
+#include "dkdv_gs.hpp"
+
+namespace bps {
+
 // ------------------------------------------------------------ launchers
+
+// The gradient-split dK/dV kernel addresses Q and dO of one batch row with
+// 32-bit buffer offsets: every byte of a row's tensor must lie within 2 GB
+// of its start.
+inline bool gs_offsets_fit(const BwdArgs& a, int dqk, int dv) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t q = ((int64_t)(a.s.Hq - 1) * a.sq.h + (int64_t)(a.s.Sq - 1) * a.sq.t + dqk) * 2;
+  const int64_t o = ((int64_t)(a.s.Hq - 1) * a.so.h + (int64_t)(a.s.Sq - 1) * a.so.t + dv) * 2;
+  return a.sq.h >= 0 && a.sq.t >= 0 && a.so.h >= 0 && a.so.t >= 0 && q < lim && o < lim;
+}
 
 // Head pairs (GQA) in the forward and dQ; BPS_HEAD_PAIRS=0 in the
 // environment keeps one head per workgroup (for comparison).
@@ -1799,6 +1815,17 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
     }
   } else if constexpr (DkvWsCfg<T, DQK, DV>::ENABLED) {
     static_assert(DkvWsCfg<T, DQK, DV>::BN == DkvCfg<T, DQK, DV>::BN, "same key tiling");
+    if constexpr (!VAR && sizeof(T) == 2 && DkvGsCfg<DQK, DV>::ENABLED) {
+      // Gradient-split kernel for GQA groups (same-host A/B, dK/dV: 2.46 against
+      // 2.52-2.55 ms on the 8K causal GQA workload; without a group to walk it
+      // was slower: 0.163 against 0.155 ms on BSHD 2K, 65.0 against 62.2 ms on
+      // the 18,900 x 75,600 shard, and no faster on packed 8K).
+      static_assert(DkvGsCfg<DQK, DV>::BN == DkvCfg<T, DQK, DV>::BN, "same key tiling");
+      if (!split && a.s.Hq / a.s.Hkv >= 2 && gs_offsets_fit(a, DQK, DV)) {
+        hipLaunchKernelGGL((attn_bwd_dkdv_gs_kernel<DQK, DV>), dim3(nws), dim3(512), 0, st, a);
+        return hipGetLastError();
+      }
+    }
     if (split)
       hipLaunchKernelGGL((attn_bwd_dkdv_ws_kernel<T, DQK, DV, VAR, false, true>), dim3(nws), dim3(512), 0, st, a);
     else
