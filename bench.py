@@ -42,7 +42,7 @@ PEAK_FP32_TFLOPS = 157.3
 METRIC = "fwd+bwd attention TFLOP/s (bf16) and % of MI355X MFMA peak, 1 GPU"
 DEFAULT_WORKLOAD = "gqa_causal_8k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["bps_common.hpp", "lds_tile.hpp", "attn_kernels.hpp", "attn_inst.hip"]
+KERNEL_SOURCES = ["bps_common.hpp", "lds_tile.hpp", "attn_kernels.hpp", "dkdv_gs.hpp", "attn_inst.hip"]
 
 
 # ------------------------------------------------------------------ counting
@@ -167,7 +167,8 @@ def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
         def t(x):
             return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
         seg = bps.Segments(t(sg["ids_q"]), t(sg.get("pos_q")), t(sg.get("ids_kv")), t(sg.get("pos_kv")))
-    fwd = bps.FwdPlan(dev["q"], dev["k"], dev["v"], causal=w.causal, segments=seg, **fwd_var)
+    fwd = bps.FwdPlan(dev["q"], dev["k"], dev["v"], causal=w.causal, segments=seg, flags=flags & ~bps.ATTN_FUSED_BWD,
+                      **fwd_var)
     bwd = bps.BwdPlan(dev["q"], dev["k"], dev["v"], fwd.o, fwd.lse, dev["do"], causal=w.causal, segments=seg,
                       flags=flags, **bwd_var)
     stream = torch.cuda.current_stream()
@@ -190,6 +191,10 @@ def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
 
     for _ in range(warmup):
         step()
+    # The route each batch row took on the device (the metadata check may
+    # send a row that the host requested on the fast route to the general
+    # one); read once, before the timed region.
+    rows = bps.route_counts(bwd.route_rows()) if warmup > 0 else None
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -207,7 +212,9 @@ def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
         phases["step"].append(ev[0].elapsed_time(ev[4]))
     avg = {k: float(np.mean(v)) for k, v in phases.items()}
     med = {k: float(np.median(v)) for k, v in phases.items()}
-    return case, wall, avg, med, fwd.route
+    if rows is None:
+        rows = bps.route_counts(bwd.route_rows())
+    return case, wall, avg, med, (fwd.route, rows)
 
 
 def ring_bench(w, cp, steps, warmup, seed=0):
@@ -291,7 +298,20 @@ def cpu_baseline(w, case, n_alg_per_head_flops, budget_s=15.0):
     return {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{w.name}: forward+backward of {len(heads)} of {w.Hq} query heads "
                       f"(batch rows all{rows_note}), {t_total:.1f} s, fp64 NumPy",
+            "cpu": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "seconds": t_total}
+
+
+def cpu_model() -> str:
+    """Model name of the host CPU (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------ counter calibration
@@ -370,6 +390,9 @@ def main():
     ap.add_argument("--fused-bwd", action="store_true",
                     help="time the single-pass backward (ATTN_FUSED_BWD): the dK/dV kernel also writes dQ "
                          "partials, the dQ phase sums them in key-tile order")
+    ap.add_argument("--force-general", action="store_true",
+                    help="set ATTN_FORCE_GENERAL: run workloads with segment metadata on the general route even "
+                         "where the fast route applies (what the fast path saves)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -410,8 +433,9 @@ def main():
     if args.fused_bwd and set(variant) - {"sink", "max_logit"}:
         raise SystemExit("--fused-bwd takes no bias or soft cap")
     import bwd_packed_segments_amd as bps
-    case, wall, avg, med, route = run_gpu(w, args.steps, args.warmup, variant=variant,
-                                          flags=bps.ATTN_FUSED_BWD if args.fused_bwd else 0)
+    flags = (bps.ATTN_FUSED_BWD if args.fused_bwd else 0) | (bps.ATTN_FORCE_GENERAL if args.force_general else 0)
+    case, wall, avg, med, (route_req, route_rows) = run_gpu(w, args.steps, args.warmup, variant=variant, flags=flags)
+    route = next(iter(route_rows)) if len(route_rows) == 1 else "mixed"
     n = allowed_pairs(w, case["segments"])
     F = flops(w, n)
     f_step = F["fwd"] + F["bwd"]
@@ -465,6 +489,7 @@ def main():
         "data": "synthetic (seeded iid N(0,1) tensors, seed 0)",
         "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "metadata": w.meta, "route": route,
+                   "route_requested": route_req, "route_rows": route_rows,
                    "allowed_pairs": n, "flop_per_step": f_step},
         "pct_peak": round(100.0 * value / peak, 2),
         "phase_ms": {k: round(v, 4) for k, v in avg.items()},
@@ -476,6 +501,10 @@ def main():
         out["config"]["variants"] = {"list": list(variant), "softcap": VARIANT_SOFTCAP if "softcap" in variant else 0,
                                      "bias": "[B, Hq, Sq, Skv] per batch row, N(0,1)" if "bias" in variant else None}
         args.no_cpu_baseline = True      # the baseline line is the plain workload's
+    if args.force_general:
+        out["metric"] = out["metric"] + " (general route forced)"
+        out["config"]["force_general"] = True
+        args.no_cpu_baseline = True
     if args.fused_bwd:
         out["metric"] = out["metric"] + " (single-pass backward)"
         out["config"]["backward"] = "single pass: dK/dV kernel with dQ partials, then a key-tile-ordered dQ sum"

@@ -31,5 +31,6 @@ from .binding import (  # noqa: F401
     fwd_workspace_size,
     lib,
     library_path,
+    route_counts,
     validate_fwd,
 )

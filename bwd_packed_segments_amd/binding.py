@@ -31,7 +31,7 @@ STATUS_NAMES = {
 EXPORTS = ("attn_fwd_workspace_size", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_phase",
            "attn_debug_mask", "attn_ring_fwd_workspace_size", "attn_ring_bwd_workspace_size", "attn_ring_fwd",
            "attn_ring_bwd", "attn_fwd_ex_workspace_size", "attn_bwd_ex_workspace_size", "attn_fwd_ex",
-           "attn_bwd_ex", "attn_bwd_ex_phase", "attn_last_error", "attn_version")
+           "attn_bwd_ex", "attn_bwd_ex_phase", "attn_route_rows", "attn_last_error", "attn_version")
 ATTN_BWD_PREPARE, ATTN_BWD_DKDV, ATTN_BWD_DQ, ATTN_BWD_ALL = 1, 2, 4, 7
 
 
@@ -121,6 +121,8 @@ def lib():
         L.attn_bwd_ex_phase.argtypes = [ctypes.c_int32, dp, sp, varp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                         vp, i32p]
         L.attn_bwd_ex_phase.restype = ctypes.c_int
+        L.attn_route_rows.argtypes = [dp, sp, vp, sz, vp, vp]
+        L.attn_route_rows.restype = ctypes.c_int
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         L.attn_version.argtypes = []
@@ -229,11 +231,30 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _route_rows(desc, csp, ws, device, stream):
+    """Device int32 [B]: the route each batch row took in the last call that
+    used workspace ws with this descriptor (attn_route_rows)."""
+    import torch
+    out = torch.empty((desc.B,), dtype=torch.int32, device=device)
+    _check(lib().attn_route_rows(ctypes.byref(desc), csp, ws.data_ptr() if ws is not None else None,
+                                 ws.numel() if ws is not None else 0, out.data_ptr(), stream))
+    return out
+
+
+def route_counts(rows) -> dict:
+    """{route name: number of batch rows} of a route_rows tensor (synchronises)."""
+    vals = rows.cpu().tolist()
+    return {name: sum(1 for r in vals if r == code) for code, name in ROUTE_NAMES.items() if code in vals}
+
+
 # ------------------------------------------------------------------ public API
 
 def attn_fwd(q, k, v, *, causal=False, scale=None, segments: Segments | None = None, flags=0, out=None,
-             return_route=False):
-    """O [B,Sq,Hq,Dv] and LSE [B,Hq,Sq] (fp32) of fused attention."""
+             return_route=False, return_route_rows=False):
+    """O [B,Sq,Hq,Dv] and LSE [B,Hq,Sq] (fp32) of fused attention.  With
+    return_route, also the route the host requested ("dense", "fast",
+    "general"); with return_route_rows, also the device int32 [B] routes
+    the batch rows took (a row may fall back from fast to general)."""
     import torch
     _require_device(q, k, v)
     B, Sq, Hq, _ = q.shape
@@ -249,9 +270,12 @@ def attn_fwd(q, k, v, *, causal=False, scale=None, segments: Segments | None = N
     route = ctypes.c_int32(-1)
     _check(L.attn_fwd(ctypes.byref(desc), csp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                       lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device), ctypes.byref(route)))
+    res = (o, lse)
     if return_route:
-        return o, lse, ROUTE_NAMES[route.value]
-    return o, lse
+        res += (ROUTE_NAMES[route.value],)
+    if return_route_rows:
+        res += (_route_rows(desc, csp, ws, q.device, _stream(q.device)),)
+    return res
 
 
 def attn_bwd(q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segments | None = None, flags=0):
@@ -318,6 +342,12 @@ class FwdPlan:
         self.route = ROUTE_NAMES[route.value]
         return self.o, self.lse
 
+    def route_rows(self, stream=None):
+        """Device int32 [B]: the route each batch row took in the last run()."""
+        q = self.t[0]
+        st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(q.device)
+        return _route_rows(self.desc, self.csp, self.ws, q.device, st)
+
 
 class BwdPlan:
     """A backward prepared once for fixed tensors, whose phases can be
@@ -360,6 +390,13 @@ class BwdPlan:
         else:
             _check(lib().attn_bwd_phase(phases, ctypes.byref(self.desc), self.csp, *args))
         return self.dq, self.dk, self.dv
+
+    def route_rows(self, stream=None):
+        """Device int32 [B]: the route each batch row took in the last run()
+        that included the PREPARE phase."""
+        q = self.t[0]
+        st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(q.device)
+        return _route_rows(self.desc, self.csp, self.ws, q.device, st)
 
 
 def attn_debug_mask(*, B, Sq, Skv, causal=False, segments: Segments | None = None, flags=0, device="cuda"):

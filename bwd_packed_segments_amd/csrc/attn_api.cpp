@@ -63,6 +63,26 @@ attn_status check_strides(const char* name, const attn_strides& s, int vec) {
   return ATTN_OK;
 }
 
+// A tensor the library writes (O; dQ, dK, dV, which take the strides of Q,
+// K, V) must not map two elements to one address, or several workgroups
+// would store to the same memory.  With the head dim contiguous, that holds
+// when the outer axes, taken in increasing stride, each step over the whole
+// span of the axes inside them (axes of extent 1 aside).
+attn_status check_disjoint(const char* name, const attn_strides& s, int B, int S, int H, int D) {
+  struct Ax { int64_t stride; int64_t ext; } ax[3] = {{s.batch, B}, {s.token, S}, {s.head, H}};
+  std::sort(ax, ax + 3, [](const Ax& x, const Ax& y) { return x.stride < y.stride; });
+  int64_t span = D;   // elements covered by the axes inside the current one
+  for (const Ax& a : ax) {
+    if (a.ext <= 1) continue;
+    if (a.stride < span)
+      return fail(ATTN_E_UNSUPPORTED, "%s strides (batch %lld, token %lld, head %lld) overlap: the library writes "
+                  "through them (outputs must not alias)", name, (long long)s.batch, (long long)s.token,
+                  (long long)s.head);
+    span = a.stride * (a.ext - 1) + span;
+  }
+  return ATTN_OK;
+}
+
 attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
   if (!d) return fail(ATTN_E_INVALID, "desc is NULL");
   if (d->B < 1 || d->Sq < 0 || d->Skv < 0 || d->Hq < 1 || d->Hkv < 1 || d->Dqk < 1 || d->Dv < 1)
@@ -88,6 +108,7 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
   if ((st = check_strides("k", d->k, vec)) != ATTN_OK) return st;
   if ((st = check_strides("v", d->v, vec)) != ATTN_OK) return st;
   if ((st = check_strides("o", d->o, vec)) != ATTN_OK) return st;
+  if ((st = check_disjoint("o (and dO)", d->o, d->B, d->Sq, d->Hq, d->Dv)) != ATTN_OK) return st;
   p->scale = d->scale == 0.f ? 1.f / std::sqrt(static_cast<float>(d->Dqk)) : d->scale;
 
   p->meta = seg != nullptr;
@@ -144,11 +165,7 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
   // (Cross 4K, 256 key tiles: 0.92 / 0.73 / 0.62 / 0.73 ms for 1 / 2 / 3 / 4
   // parts.)
   const size_t n_kt = ((size_t)d->Skv + 127) / 128, nkvb = (size_t)d->B * d->Hkv * n_kt;
-  int split = (nkvb > 0 && nkvb < 512) ? (int)std::min<size_t>(4, std::max<size_t>(2, (768 + nkvb / 2) / nkvb)) : 1;
-  if (const char* e = getenv("BPS_KV_SPLIT")) {   // comparison switch: force 1-4 parts
-    const int f = atoi(e);
-    if (f >= 1 && f <= 4) split = f;
-  }
+  const int split = (nkvb > 0 && nkvb < 512) ? (int)std::min<size_t>(4, std::max<size_t>(2, (768 + nkvb / 2) / nkvb)) : 1;
   if (d->dtype == ATTN_BF16 && nkvb > 0 && split > 1) {
     p->kv_split = split;
     p->off_dkvp = off;
@@ -582,6 +599,12 @@ attn_status bwd_impl(int32_t phases, const attn_desc* d, const attn_segments* se
         (st = check_align("dout", dout, d->dtype)) || (st = check_align("dq", dq, d->dtype)) ||
         (st = check_align("dk", dk, d->dtype)) || (st = check_align("dv", dv, d->dtype)))
       return st;
+    if ((phases & ATTN_BWD_DQ) && (st = check_disjoint("q (and dQ)", d->q, d->B, d->Sq, d->Hq, d->Dqk)) != ATTN_OK)
+      return st;
+    if ((phases & ATTN_BWD_DKDV) &&
+        ((st = check_disjoint("k (and dK)", d->k, d->B, d->Skv, d->Hkv, d->Dqk)) != ATTN_OK ||
+         (st = check_disjoint("v (and dV)", d->v, d->B, d->Skv, d->Hkv, d->Dv)) != ATTN_OK))
+      return st;
     if ((st = check_ws(workspace, workspace_bytes, vp.ws_bwd)) != ATTN_OK) return st;
     if (route_out) *route_out = route_of(p);
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -726,6 +749,23 @@ attn_status attn_debug_mask(const attn_desc* d, const attn_segments* seg, uint8_
   }
 }
 
+attn_status attn_route_rows(const attn_desc* d, const attn_segments* seg, const void* workspace,
+                            size_t workspace_bytes, int32_t* route_rows, void* stream) {
+  try {
+    Plan p;
+    attn_status st = make_plan(d, seg, &p);
+    if (st != ATTN_OK) return st;
+    if (need_nonnull(route_rows, d->B)) return fail(ATTN_E_INVALID, "route_rows must not be NULL");
+    if (p.meta && (st = check_ws(const_cast<void*>(workspace), workspace_bytes, p.ws_fwd)) != ATTN_OK) return st;
+    const int* src = p.meta ? reinterpret_cast<const int*>(static_cast<const char*>(workspace) + p.off_route) : nullptr;
+    hipError_t e = bps::launch_route_rows(src, d->B, route_rows, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "route copy launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
+}
+
 size_t attn_ring_fwd_workspace_size(const attn_desc* desc, const attn_segments* seg, int32_t cp) {
   RingPlan rp;
   return make_ring_plan(desc, seg, cp, false, &rp) == ATTN_OK ? rp.ws : 0;
@@ -799,6 +839,10 @@ attn_status attn_ring_bwd(const attn_desc* d, const attn_segments* seg, int32_t 
         (st = check_align("v", v, d->dtype)) || (st = check_align("o", o, d->dtype)) ||
         (st = check_align("dout", dout, d->dtype)) || (st = check_align("dq", dq, d->dtype)) ||
         (st = check_align("dk", dk, d->dtype)) || (st = check_align("dv", dv, d->dtype)))
+      return st;
+    if ((st = check_disjoint("q (and dQ)", d->q, d->B, d->Sq, d->Hq, d->Dqk)) != ATTN_OK ||
+        (st = check_disjoint("k (and dK)", d->k, d->B, d->Skv, d->Hkv, d->Dqk)) != ATTN_OK ||
+        (st = check_disjoint("v (and dV)", d->v, d->B, d->Skv, d->Hkv, d->Dv)) != ATTN_OK)
       return st;
     if ((st = check_ws(workspace, workspace_bytes, rp.ws)) != ATTN_OK) return st;
     if (d->Sq == 0 && d->Skv == 0) return ATTN_OK;

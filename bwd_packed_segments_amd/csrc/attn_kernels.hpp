@@ -1745,16 +1745,6 @@ inline bool gs_offsets_fit(const BwdArgs& a, int dqk, int dv) {
   return a.sq.h >= 0 && a.sq.t >= 0 && a.so.h >= 0 && a.so.t >= 0 && q < lim && o < lim;
 }
 
-// Head pairs (GQA) in the forward and dQ; BPS_HEAD_PAIRS=0 in the
-// environment keeps one head per workgroup (for comparison).
-inline bool fwd_head_pairs() {
-  static const bool on = [] {
-    const char* e = getenv("BPS_HEAD_PAIRS");
-    return !(e && e[0] == '0');
-  }();
-  return on;
-}
-
 template <typename T, int DQK, int DV, int VM>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<T, DQK, DV>;
@@ -1762,7 +1752,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
   if constexpr (VM == 0 && FwdCfg<T, DQK, DV, 8>::WIDE_OK) {
-    if ((a.s.Hq / a.s.Hkv) % 2 == 0 && fwd_head_pairs()) {
+    if ((a.s.Hq / a.s.Hkv) % 2 == 0) {   // head pairs of a GQA group
       using C8 = FwdCfg<T, DQK, DV, 8, 2>;
       const long long nb8 = (long long)a.s.B * (a.s.Hq / 2) * ((a.s.Sq + C8::BM - 1) / C8::BM);
       hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, 0, 8, 2>), dim3((unsigned)nb8), dim3(C8::THREADS), 0, st, a);
@@ -1858,7 +1848,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   const long long nblocks = (long long)a.s.B * a.s.Hq * n_qt;
   if (nblocks <= 0) return hipSuccess;
   if constexpr (!VAR && DqCfg<T, DQK, DV, 8>::WIDE_OK) {
-    if ((a.s.Hq / a.s.Hkv) % 2 == 0 && fwd_head_pairs()) {
+    if ((a.s.Hq / a.s.Hkv) % 2 == 0) {   // head pairs of a GQA group
       using C8 = DqCfg<T, DQK, DV, 8, 2>;
       const long long nb8 = (long long)a.s.B * (a.s.Hq / 2) * ((a.s.Sq + C8::BM - 1) / C8::BM);
       hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV, false, 8, 2>), dim3((unsigned)nb8), dim3(C8::THREADS), 0, st,

@@ -147,6 +147,8 @@ hipError_t launch_ring_reduce(int dtype_bf16, const RingReduceArgs& a, hipStream
 // result of hipGetLastError() after its launches.
 hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st);
 hipError_t launch_debug_mask(const MaskArgs& a, hipStream_t st);
+// out[b] = route[b] for b < B (route NULL: kRouteDense everywhere).
+hipError_t launch_route_rows(const int* route, int B, int* out, hipStream_t st);
 
 // VAR / VM select the kernels that apply the variants of VarView (forward
 // VM: 0 plain, 1 sink and max logit only, 2 bias or soft cap as well).

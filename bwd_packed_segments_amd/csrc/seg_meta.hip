@@ -217,7 +217,20 @@ __global__ __launch_bounds__(256) void debug_mask_kernel(MaskArgs a) {
   }
 }
 
+// The route each batch row took (route NULL: no metadata, every row dense).
+__global__ __launch_bounds__(256) void route_rows_kernel(const int* route, int B, int* out) {
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < B; b += gridDim.x * blockDim.x)
+    out[b] = route ? route[b] : kRouteDense;
+}
+
 }  // namespace
+
+hipError_t launch_route_rows(const int* route, int B, int* out, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  const int blocks = (B + 255) / 256 < 1024 ? (B + 255) / 256 : 1024;
+  hipLaunchKernelGGL(route_rows_kernel, dim3(blocks), dim3(256), 0, st, route, B, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st) {
   dim3 grid(a.B, a.sides);

@@ -47,7 +47,12 @@
  * elements, the head-dim axis contiguous).  dQ, dK, dV use the strides of
  * Q, K, V; dO uses the strides of O (the output gradient must share the
  * saved output's layout, the one-GPU form of the sharding alignment in
- * PR 3516, Changes 1).  LSE is [B, Hq, Sq] fp32, contiguous.  Segment
+ * PR 3516, Changes 1).  Packed buffers pass as strided views: Q, K, V of a
+ * [B, S, 3, H, D] buffer, or K, V of [B, S, 2, Hkv, D], with the token
+ * stride spanning the whole packed row (TransformerEngine PR 2358, review of
+ * the KV-packed stride).  Strides the library writes through (O, and for
+ * the backward Q, K, V, which dQ, dK, dV share) must not overlap, i.e. no
+ * two elements at one address: otherwise ATTN_E_UNSUPPORTED.  LSE is [B, Hq, Sq] fp32, contiguous.  Segment
  * metadata are int32 [B, S], contiguous.
  *
  * Memory and streams.  Every pointer argument except route_out is device
@@ -114,7 +119,9 @@ enum {
  * cap (ATTN_E_UNSUPPORTED otherwise); the ring emulation does not take it.
  * attn_fwd ignores the flag. */
 
-/* Route reported through route_out. */
+/* Routes.  route_out (host) receives the route the host requested for the
+ * call; attn_route_rows (below) gives the route each batch row took on the
+ * device, which may fall back from fast to general. */
 enum {
   ATTN_ROUTE_DENSE = 0,    /* no metadata: plain or causal mask           */
   ATTN_ROUTE_FAST = 1,     /* fast route requested; a batch row whose
@@ -204,6 +211,25 @@ attn_status attn_bwd_phase(int32_t phases, const attn_desc* desc, const attn_seg
 attn_status attn_debug_mask(const attn_desc* desc, const attn_segments* seg,
                             uint8_t* mask_out, int32_t* route_rows,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* The route each batch row took in the last attn_fwd, attn_bwd(_phase),
+ * attn_*_ex or attn_debug_mask call that used this workspace with the same
+ * descriptor and metadata: route_rows[b] (int32 [B], device) = 0 dense,
+ * 1 fast, 2 general.  The host requests the fast route when Q and KV
+ * metadata are shared or, for equal lengths, may match; the metadata kernel
+ * then checks each row (matching metadata, contiguous increasing runs,
+ * positions equal to run offsets) and runs the general route where the check
+ * fails.  This call reports that outcome without a synchronisation: it
+ * enqueues one small kernel on `stream` that copies the per-row routes out
+ * of the workspace, so it must be ordered after the call it reports on and
+ * before the workspace is reused.  The TransformerEngine page on fused
+ * attention sharding (PR 3516, review) asks that a caller can tell when the
+ * fast path is not taken; this is that report.  Without metadata every row
+ * is 0 and the workspace is not read (it may be NULL).  Needs at least
+ * attn_fwd_workspace_size bytes of workspace when seg is given. */
+attn_status attn_route_rows(const attn_desc* desc, const attn_segments* seg,
+                            const void* workspace, size_t workspace_bytes,
+                            int32_t* route_rows, void* stream);
 
 /* One-GPU emulation of ring (context-parallel) attention, the long-sequence
  * scheme of the maxdiffusion ring-attention backward page (Summary and Key

@@ -276,3 +276,50 @@ def test_split_dkdv_workspace():
     wide = good(B=1, Sq=4096, Skv=4096, Hq=48, Hkv=12, Dqk=128)  # 384 key tiles -> 2 parts
     extra = B.bwd_workspace_size(wide) - 2 * 48 * 4096 * 4
     assert 384 * 2 * 128 * 256 * 4 <= extra < 384 * 2 * 128 * 256 * 4 + 1024
+
+
+def test_overlapping_output_strides_rejected():
+    """Strides the library writes through must not alias: O in both calls,
+    and Q, K, V in the backward (dQ, dK, dV share them).  An expanded K
+    (head stride 0 over two KV heads) may be read, but its gradient would be
+    stored by several workgroups to the same memory."""
+    d = good(o=(300 * 4 * 128, 64, 128))                    # token stride 64 < head span 4 x 128
+    st, text = B.validate_fwd(d)
+    assert st == B.ATTN_E_UNSUPPORTED and "overlap" in text
+    st, text = B.validate_bwd(d)
+    assert st == B.ATTN_E_UNSUPPORTED and "overlap" in text
+    d = good(k=(300 * 128, 128, 0))                         # both KV heads at one address
+    st, text = B.validate_bwd(d)
+    assert st == B.ATTN_E_UNSUPPORTED and "k (and dK)" in text
+    d = good(q=(0, 4 * 128, 128))                           # both batch rows at one address
+    st, text = B.validate_bwd(d)
+    assert st == B.ATTN_E_UNSUPPORTED and "q (and dQ)" in text
+    d = good(v=(300 * 2 * 128, 2 * 128, 128), B=2, Hkv=2)   # disjoint: validation reaches the workspace check
+    st, text = B.validate_bwd(d)
+    assert st == B.ATTN_E_WORKSPACE, text
+
+
+def test_disjoint_packed_views_pass_the_stride_check():
+    """Packed QKV [B, S, 3, H, D] and KV [B, S, 2, Hkv, D] views are disjoint
+    per tensor: validation passes the stride checks and stops at the missing
+    workspace, which is checked after them."""
+    S, H, D = 300, 4, 128
+    qkv = (S * 3 * H * D, 3 * H * D, D)
+    kv = (S * 2 * 2 * D, 2 * 2 * D, D)
+    d = good(q=qkv, k=kv, v=kv, o=(S * H * D, H * D, D))
+    st, text = B.validate_bwd(d)
+    assert st == B.ATTN_E_WORKSPACE, text
+
+
+def test_route_rows_validation():
+    L = B.lib()
+    seg = B.attn_segments(0x1000, None, None, None)
+    d = good()
+    st = L.attn_route_rows(ctypes.byref(d), ctypes.byref(seg), 1 << 20, 1 << 20, None, None)
+    assert st == B.ATTN_E_INVALID and b"route_rows" in L.attn_last_error()
+    need = B.fwd_workspace_size(d, seg)
+    st = L.attn_route_rows(ctypes.byref(d), ctypes.byref(seg), 1 << 20, need - 1, 1 << 12, None)
+    assert st == B.ATTN_E_WORKSPACE
+    bad = good(Hq=3)
+    st = L.attn_route_rows(ctypes.byref(bad), None, None, 0, 1 << 12, None)
+    assert st == B.ATTN_E_INVALID

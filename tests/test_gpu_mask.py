@@ -173,3 +173,76 @@ def test_dk_zero_sum_per_segment():
         tot = gpu["dK"][0, idx].sum(axis=0)
         scale = np.abs(gpu["dK"][0, idx]).sum(axis=0) + 1e-6
         assert np.max(np.abs(tot) / scale) < 0.05
+
+
+def _long_row_metadata():
+    """Two rows of 8192 + 3000 tokens, longer than one 8192-token scan round
+    of the metadata kernel.  Row 0: packed segments with one run straddling
+    token 8192 (fast-route eligible).  Row 1: the same, but the id of an
+    early run appears again after token 8192 (not eligible: the general
+    route must take it)."""
+    S = 8192 + 3000
+    cuts = [0, 700, 2500, 2600, 5000, 7900, 8500, 9000, 10400, 11100]   # run [7900, 8500) straddles 8192
+    ids = np.zeros((2, S), dtype=np.int32)
+    for r, (a, b) in enumerate(zip(cuts[:-1], cuts[1:])):
+        ids[:, a:b] = r + 1
+    ids[:, 11100:] = 0                      # padded tail
+    ids[1, 9000:9100] = 2                    # id 2 again, in the second round
+    return S, {"ids_q": ids, "pos_q": oracle.derive_pos(ids)}
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_rows_across_scan_rounds(causal):
+    """Metadata rows longer than one scan round of the metadata kernel: the
+    run bounds and summaries carried from one round to the next give the
+    oracle's mask bit for bit, and each row takes the route the oracle's
+    eligibility test names (fast for row 0, general for row 1)."""
+    import bwd_packed_segments_amd as bps
+    import torch
+    S, seg = _long_row_metadata()
+    print(f"[mask] long rows S={S} causal={causal}", flush=True)
+    mask, routes = bps.attn_debug_mask(B=2, Sq=S, Skv=S, causal=causal, segments=G.seg_to_dev(seg))
+    torch.cuda.synchronize()
+    elig = oracle.fast_route_eligible(seg, 2, S, S)
+    assert list(elig) == [True, False]
+    assert routes.cpu().tolist() == [1, 2]
+    rs = oracle.resolve_segments(seg, 2, S, S)
+    for b in range(2):
+        ref = oracle.allowed_mask(b, S, S, causal, rs)
+        got = mask[b].cpu().numpy().astype(bool)
+        assert np.array_equal(got, ref), f"row {b}: {np.count_nonzero(got != ref)} mask bits differ"
+
+
+def _repeating_meta(S, period, n_ids):
+    """Ids 1..n_ids, a new id every `period` tokens, repeating over the whole
+    row (each id in many separate runs: general route); positions from the
+    index."""
+    idx = np.arange(S)
+    ids = ((idx // period) % n_ids + 1).astype(np.int32)[None, :]
+    return ids, idx.astype(np.int32)[None, :]
+
+
+@pytest.mark.parametrize("Sq,Skv,Hq,Hkv", [(70_000, 512, 2, 1), (70_000, 512, 1, 1), (512, 70_000, 2, 1)],
+                         ids=["long_q_gqa", "long_q", "long_kv"])
+def test_walks_longer_than_class_table(Sq, Skv, Hq, Hkv):
+    """Walks of more than 1024 tiles (the per-workgroup table of tile classes
+    holds the first 1024; later tiles are classified on the fly): 70,000
+    queries against 512 keys make the dK/dV walks that long, 512 queries
+    against 70,000 keys the forward and dQ walks.  Cross-attention metadata
+    whose ids repeat all along both rows (general route), non-causal, against
+    the oracle.  The 70,000-token rows also span nine scan rounds of the
+    metadata kernel."""
+    w = inputs.workload("thd_cross_ring_4k", Sq=Sq, Skv=Skv, Hq=Hq, Hkv=Hkv, Dqk=64, Dv=64)
+    case = inputs.make_case(w, 5)
+    # 20 query ids against 5 key ids: each key is attended by one query in
+    # twenty (about 7,000 terms per dK/dV element on the long query row,
+    # whose ids 6..20 match nothing, so those tiles are skipped), which keeps
+    # the reductions at the length of the workloads' own.
+    iq, pq = _repeating_meta(Sq, 600, 20)
+    ik, pk = _repeating_meta(Skv, 100, 5)
+    case["segments"] = {"ids_q": iq, "pos_q": pq, "ids_kv": ik, "pos_kv": pk}
+    print(f"[parity] long walks Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv}", flush=True)
+    gpu = G.numpy_out(G.run_gpu(case))
+    assert gpu["route"] == "general"
+    ref = G.run_oracle(case)
+    G.check_all(case, gpu, ref)

@@ -164,19 +164,98 @@ def test_single_token():
 # ------------------------------------------------------------ full sizes
 
 FULL = [
-    ("bshd_causal_2k", [0, 15]),
-    ("thd_packed_8k", [0, 31]),
-    ("gqa_causal_8k", list(range(8))),      # whole group of KV head 0
-    ("thd_cross_ring_4k", list(range(4))),  # whole group of KV head 0
+    ("bshd_causal_2k", [0, 15], 0),
+    ("thd_packed_8k", [0, 31], 0),
+    ("gqa_causal_8k", list(range(8)), 0),      # whole group of KV head 0
+    ("gqa_causal_8k", list(range(56, 64)), 1),  # whole group of KV head 7
+    ("gqa_causal_8k", list(range(24, 32)), 2),  # whole group of KV head 3
+    ("thd_cross_ring_4k", list(range(4)), 0),  # whole group of KV head 0
+    ("thd_cross_ring_4k", list(range(28, 32)), 1),
+    ("thd_cross_ring_4k", list(range(12, 16)), 2),
 ]
 
 
-@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled_heads(name, heads):
+@pytest.mark.parametrize("name,heads,seed", FULL, ids=[f"{f[0]}-seed{f[2]}" for f in FULL])
+def test_full_size_sampled_heads(name, heads, seed):
     """The benchmark workloads at full size, in the launch configuration the
-    bench times; the oracle computes a sample of heads exactly."""
-    case = inputs.make_case(name, 0)
+    bench times; the oracle computes a sample of heads exactly (for dK/dV a
+    whole GQA group), three seeds for the GQA and cross workloads."""
+    case = inputs.make_case(name, seed)
     _parity(case, heads=heads)
+
+
+EXPECTED_ROUTE = {"thd_packed_8k": "fast", "thd_cross_ring_4k": "general", "gqa_causal_8k": "dense",
+                  "bshd_causal_2k": "dense"}
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("name", sorted(EXPECTED_ROUTE))
+def test_effective_route_full_size(name, seed):
+    """The route each batch row takes on the device at full size: every row
+    of the packed workload on the fast route (every row is eligible), every
+    row of the cross workload on the general one.  The cross workload has
+    equal lengths, so the host requests the fast route and the device check
+    turns it down: independent, rotated KV metadata must take the general
+    path (TransformerEngine PR 3516, Changes 3 and 4).  Rows agree with the
+    oracle's eligibility test, and ATTN_FORCE_GENERAL sends every row of the
+    packed workload to the general route."""
+    import oracle
+    import bwd_packed_segments_amd as bps
+    case = inputs.make_case(inputs.workload(name, Hq=inputs.WORKLOADS[name].Hkv), seed)
+    w = case["workload"]
+    print(f"[route] {name} seed={seed}", flush=True)
+    t = {k: G.to_dev(case[k], w.dtype) for k in ("q", "k", "v")}
+    seg = G.seg_to_dev(case["segments"])
+    _, _, req, rows = bps.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, segments=seg, return_route=True,
+                                   return_route_rows=True)
+    rows = rows.cpu().numpy()
+    expect = {"dense": 0, "fast": 1, "general": 2}[EXPECTED_ROUTE[name]]
+    assert np.all(rows == expect), (name, rows)
+    if case["segments"] is not None:
+        elig = oracle.fast_route_eligible(case["segments"], w.B, w.Sq, w.Skv)
+        assert np.array_equal(rows == 1, elig), (rows, elig)
+        assert req == "fast"       # shared metadata, or equal lengths that may match
+        _, _, req_g, rows_g = bps.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, segments=seg,
+                                           flags=bps.ATTN_FORCE_GENERAL, return_route=True, return_route_rows=True)
+        assert req_g == "general" and np.all(rows_g.cpu().numpy() == 2)
+    else:
+        assert req == "dense"
+
+
+def test_kv_packed_views():
+    """K and V as views into one packed [B, S, 2, Hkv, D] buffer, the
+    KV-packed layout whose V offset the TransformerEngine page on non-packed
+    common calls (PR 2358, review of the KV-packed stride) works out from the
+    value head dim; GQA, causal, ragged length."""
+    case = G.small_case("gqa_causal_8k", 12, S=333, Hq=4, Hkv=2)
+    kv = np.stack([case["k"], case["v"]], axis=2)                       # [B, S, 2, Hkv, D]
+    t = G.to_dev(kv, "bf16")
+    tensors = {"q": G.to_dev(case["q"], "bf16"), "k": t[:, :, 0], "v": t[:, :, 1], "do": G.to_dev(case["do"], "bf16")}
+    assert tensors["k"].stride()[1] == 2 * 2 * 128 and tensors["v"].data_ptr() - tensors["k"].data_ptr() == 2 * 2 * 128
+    print("[parity] kv packed views", flush=True)
+    gpu = G.numpy_out(G.run_gpu(case, tensors=tensors))
+    ref = G.run_oracle(case)
+    G.check_all(case, gpu, ref)
+
+
+def test_do_layout_must_match_o():
+    """dO must share O's strides (the output gradient takes the saved
+    output's layout, TransformerEngine PR 3516, Changes 1): a dO in another
+    layout is refused before anything runs, by attn_bwd and by BwdPlan."""
+    import torch
+    import bwd_packed_segments_amd as bps
+    case = G.small_case("gqa_causal_8k", 13, S=128, Hq=4, Hkv=2)
+    t = {k: G.to_dev(case[k], "bf16") for k in ("q", "k", "v", "do")}
+    o, lse = bps.attn_fwd(t["q"], t["k"], t["v"], causal=True)
+    do_bhsd = t["do"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)   # same shape, BHSD strides
+    assert do_bhsd.shape == o.shape and do_bhsd.stride() != o.stride()
+    with pytest.raises(ValueError, match="strides of O"):
+        bps.attn_bwd(t["q"], t["k"], t["v"], o, lse, do_bhsd, causal=True)
+    with pytest.raises(ValueError, match="strides of O"):
+        bps.BwdPlan(t["q"], t["k"], t["v"], o, lse, do_bhsd, causal=True)
+    dq, dk, dv = bps.attn_bwd(t["q"], t["k"], t["v"], o, lse, do_bhsd.contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq.float()).all()
 
 
 def test_long_shard_sampled_rows_and_sums():
@@ -214,3 +293,28 @@ def test_long_shard_sampled_rows_and_sums():
     dk_sum = gpu["dK"].sum(axis=1)
     scale = np.abs(gpu["dK"]).sum(axis=1) + 1.0
     assert np.max(np.abs(dk_sum) / scale) < 1e-2
+
+
+def test_long_shard_dkdv_elementwise():
+    """dK and dV of one head of the 18,900 x 75,600 shard, element by element.
+    Without a mask every query row's softmax is independent of the others, so
+    the oracle runs over disjoint chunks of query rows, each against all
+    75,600 keys, and each chunk's contribution to dK and dV (sums over its
+    rows) is added in fp64: that is the exact gradient, computed in pieces."""
+    case = inputs.make_case("wan_cp_shard", 0)
+    w = case["workload"]
+    print(f"[parity] {w} dK/dV head 0, all keys", flush=True)
+    gpu = G.numpy_out(G.run_gpu(case))
+    head = 0
+    dk = np.zeros((w.B, w.Skv, w.Dqk))
+    dv = np.zeros((w.B, w.Skv, w.Dv))
+    step = 1575
+    import oracle
+    for r0 in range(0, w.Sq, step):
+        ref = oracle.backward(case["q"][:, r0:r0 + step], case["k"], case["v"], case["do"][:, r0:r0 + step],
+                              causal=False, heads=[head])
+        dk += ref["dK"][:, :, head]
+        dv += ref["dV"][:, :, head]
+    tol = G.TOL["bf16"]
+    G.compare("dK", gpu["dK"][:, :, head], dk, tol)
+    G.compare("dV", gpu["dV"][:, :, head], dv, tol)
