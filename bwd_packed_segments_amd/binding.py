@@ -85,6 +85,12 @@ def lib():
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with `python -m bwd_packed_segments_amd.build` "
                                "(or __graft_entry__.build()); there is no fallback path")
+        # torch first: it carries its own HIP runtime, and the library must
+        # bind to that one.  Loaded before torch, the library would pull in
+        # the system's HIP runtime and the process would hold two (kernel
+        # launches then fail with misleading errors such as "no ROCm-capable
+        # device").
+        import torch  # noqa: F401
         L = ctypes.CDLL(path)
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         dp, sp = ctypes.POINTER(attn_desc), ctypes.POINTER(attn_segments)
