@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     FwdPlan,
     Segments,
     attn_bwd,
+    attn_bwd_noalloc,
     attn_bwd_ex,
     attn_debug_mask,
     attn_fwd,

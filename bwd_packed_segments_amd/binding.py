@@ -31,7 +31,8 @@ STATUS_NAMES = {
 EXPORTS = ("attn_fwd_workspace_size", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_phase",
            "attn_debug_mask", "attn_ring_fwd_workspace_size", "attn_ring_bwd_workspace_size", "attn_ring_fwd",
            "attn_ring_bwd", "attn_fwd_ex_workspace_size", "attn_bwd_ex_workspace_size", "attn_fwd_ex",
-           "attn_bwd_ex", "attn_bwd_ex_phase", "attn_route_rows", "attn_last_error", "attn_version")
+           "attn_bwd_ex", "attn_bwd_ex_phase", "attn_route_rows", "attn_bwd_noalloc", "attn_last_error",
+           "attn_version")
 ATTN_BWD_PREPARE, ATTN_BWD_DKDV, ATTN_BWD_DQ, ATTN_BWD_ALL = 1, 2, 4, 7
 
 
@@ -127,6 +128,8 @@ def lib():
         L.attn_bwd_ex_phase.argtypes = [ctypes.c_int32, dp, sp, varp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                         vp, i32p]
         L.attn_bwd_ex_phase.restype = ctypes.c_int
+        L.attn_bwd_noalloc.argtypes = [dp, sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32p]
+        L.attn_bwd_noalloc.restype = ctypes.c_int
         L.attn_route_rows.argtypes = [dp, sp, vp, sz, vp, vp]
         L.attn_route_rows.restype = ctypes.c_int
         L.attn_last_error.argtypes = []
@@ -306,6 +309,40 @@ def attn_bwd(q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segment
                       lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                       ws.data_ptr(), ws.numel(), _stream(q.device), None))
     return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, *, causal=False, scale=None, segments: Segments | None = None, flags=0,
+                     out=None):
+    """dQ, dK, dV through attn_bwd_noalloc: the library takes no workspace
+    and allocates nothing (its scratch is a per-GPU device array).  The
+    outputs are allocated here unless given as out=(dq, dk, dv) with the
+    strides of q, k, v."""
+    import torch
+    _require_device(q, k, v, o, lse, do)
+    if do.stride() != o.stride() or do.shape != o.shape:
+        raise ValueError("dO must have the shape and strides of O")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    if out is None:
+        out = tuple(torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device) for t in (q, k, v))
+    dq, dk, dv = out
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("dq, dk, dv must have the strides of q, k, v")
+    desc = _desc_for(q, k, v, _strides(o), causal, scale, flags)
+    cs, csp = _seg_ptr(segments)
+    _check(lib().attn_bwd_noalloc(ctypes.byref(desc), csp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                  _stream(q.device), None))
+    return dq, dk, dv
+
+
+def validate_bwd_noalloc(desc: attn_desc, segments: attn_segments | None = None, *, ptr=1 << 12):
+    """attn_bwd_noalloc with placeholder addresses, for descriptors that must
+    fail host validation (nothing may launch); returns (status, message)."""
+    L = lib()
+    st = L.attn_bwd_noalloc(ctypes.byref(desc), ctypes.byref(segments) if segments else None, ptr, ptr, ptr, ptr,
+                            ptr, ptr, ptr, ptr, ptr, None, None)
+    return st, L.attn_last_error().decode(errors="replace")
 
 
 class FwdPlan:

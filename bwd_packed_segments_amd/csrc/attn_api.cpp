@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "bps_args.hpp"
@@ -83,7 +84,7 @@ attn_status check_disjoint(const char* name, const attn_strides& s, int B, int S
   return ATTN_OK;
 }
 
-attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
+attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p, bool allow_split = true) {
   if (!d) return fail(ATTN_E_INVALID, "desc is NULL");
   if (d->B < 1 || d->Sq < 0 || d->Skv < 0 || d->Hq < 1 || d->Hkv < 1 || d->Dqk < 1 || d->Dv < 1)
     return fail(ATTN_E_INVALID, "sizes must be positive (B=%d Sq=%d Skv=%d Hq=%d Hkv=%d Dqk=%d Dv=%d)", d->B,
@@ -165,7 +166,9 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p) {
   // (Cross 4K, 256 key tiles: 0.92 / 0.73 / 0.62 / 0.73 ms for 1 / 2 / 3 / 4
   // parts.)
   const size_t n_kt = ((size_t)d->Skv + 127) / 128, nkvb = (size_t)d->B * d->Hkv * n_kt;
-  const int split = (nkvb > 0 && nkvb < 512) ? (int)std::min<size_t>(4, std::max<size_t>(2, (768 + nkvb / 2) / nkvb)) : 1;
+  const int split = (allow_split && nkvb > 0 && nkvb < 512)
+                        ? (int)std::min<size_t>(4, std::max<size_t>(2, (768 + nkvb / 2) / nkvb))
+                        : 1;
   if (d->dtype == ATTN_BF16 && nkvb > 0 && split > 1) {
     p->kv_split = split;
     p->off_dkvp = off;
@@ -532,6 +535,36 @@ bps::VarView var_view(const attn_desc* d, const attn_variant* var, const VarPlan
   return v;
 }
 
+// ------------------------------------------------------------ scratch of attn_bwd_noalloc
+
+// The workspace of attn_bwd_noalloc: a file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  Host code
+// never uses the array's name as an address: its device address is looked
+// up once per device, with that device current, and kept here.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+attn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_E_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_E_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(ATTN_E_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 attn_status fwd_impl(const attn_desc* d, const attn_segments* seg, const attn_variant* var, const void* q,
                      const void* k, const void* v, void* o, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream, int32_t* route_out) {
@@ -576,12 +609,12 @@ attn_status fwd_impl(const attn_desc* d, const attn_segments* seg, const attn_va
 attn_status bwd_impl(int32_t phases, const attn_desc* d, const attn_segments* seg, const attn_variant* var,
                      const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream,
-                     int32_t* route_out) {
+                     int32_t* route_out, bool allow_split = true, bool use_scratch = false) {
   try {
     if (phases <= 0 || (phases & ~ATTN_BWD_ALL))
       return fail(ATTN_E_INVALID, "phases must be a nonzero combination of ATTN_BWD_* bits (got %d)", phases);
     Plan p;
-    attn_status st = make_plan(d, seg, &p);
+    attn_status st = make_plan(d, seg, &p, allow_split);
     if (st != ATTN_OK) return st;
     VarPlan vp;
     if ((st = make_var_plan(d, p, var, &vp)) != ATTN_OK) return st;
@@ -605,6 +638,14 @@ attn_status bwd_impl(int32_t phases, const attn_desc* d, const attn_segments* se
         ((st = check_disjoint("k (and dK)", d->k, d->B, d->Skv, d->Hkv, d->Dqk)) != ATTN_OK ||
          (st = check_disjoint("v (and dV)", d->v, d->B, d->Skv, d->Hkv, d->Dv)) != ATTN_OK))
       return st;
+    if (use_scratch) {   // attn_bwd_noalloc: every argument checked; now the device's scratch array
+      if (vp.ws_bwd > kScratchBytes)
+        return fail(ATTN_E_WORKSPACE, "this backward needs %zu bytes of scratch; attn_bwd_noalloc holds %zu "
+                    "(B * Hq * Sq up to about 4 million rows): use attn_bwd with a workspace", vp.ws_bwd,
+                    kScratchBytes);
+      if ((st = scratch_of_current_device(&workspace)) != ATTN_OK) return st;
+      workspace_bytes = kScratchBytes;
+    }
     if ((st = check_ws(workspace, workspace_bytes, vp.ws_bwd)) != ATTN_OK) return st;
     if (route_out) *route_out = route_of(p);
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -688,6 +729,19 @@ attn_status attn_bwd(const attn_desc* d, const attn_segments* seg, const void* q
                      void* workspace, size_t workspace_bytes, void* stream, int32_t* route_out) {
   return attn_bwd_phase(ATTN_BWD_ALL, d, seg, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
                         stream, route_out);
+}
+
+attn_status attn_bwd_noalloc(const attn_desc* d, const attn_segments* seg, const void* q, const void* k,
+                             const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                             void* dv, void* stream, int32_t* route_out) {
+  try {
+    if (d && (d->flags & ATTN_FUSED_BWD))
+      return fail(ATTN_E_UNSUPPORTED, "attn_bwd_noalloc does not take ATTN_FUSED_BWD");
+    return bwd_impl(ATTN_BWD_ALL, d, seg, nullptr, q, k, v, o, lse, dout, dq, dk, dv, nullptr, 0, stream,
+                    route_out, /*allow_split=*/false, /*use_scratch=*/true);
+  } catch (...) {
+    return fail(ATTN_E_DEVICE, "unexpected host exception");
+  }
 }
 
 size_t attn_fwd_ex_workspace_size(const attn_desc* desc, const attn_segments* seg, const attn_variant* var) {

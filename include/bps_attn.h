@@ -180,6 +180,29 @@ attn_status attn_bwd(const attn_desc* desc, const attn_segments* seg,
                      void* workspace, size_t workspace_bytes,
                      void* stream, int32_t* route_out);
 
+/* attn_bwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same backward
+ * with no workspace argument.  Its scratch (segment metadata, Delta, LSE in
+ * base 2) lives in a file-scope device array of 32 MiB that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  It runs on
+ * the current device, which must be the one the stream and tensors belong
+ * to.  Limits: the workspace attn_bwd would need without split dK/dV walks
+ * must fit in 32 MiB (B * Hq * Sq up to about 4 million rows), otherwise
+ * ATTN_E_WORKSPACE; ATTN_FUSED_BWD is ATTN_E_UNSUPPORTED.  Small grids that
+ * attn_bwd splits into partial walks run unsplit here, so results equal
+ * attn_bwd's bitwise when attn_bwd does not split (at least 512 key tiles of
+ * 128) and within rounding otherwise.  Every call on one GPU uses that GPU's
+ * one array and nothing in it needs to start at zero (each call writes what
+ * it reads); calls that overlap on one GPU, on different streams or
+ * threads, race on it and must be ordered by the caller.  Tensors, strides,
+ * ownership, streams and errors otherwise as attn_bwd. */
+attn_status attn_bwd_noalloc(const attn_desc* desc, const attn_segments* seg,
+                             const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv,
+                             void* stream, int32_t* route_out);
+
 /* Backward in phases, for callers that time or overlap them.  phases is a
  * nonzero OR of the bits below; ATTN_BWD_ALL is attn_bwd.  PREPARE (segment
  * metadata scan, Delta = rowsum(dO * O), LSE in base 2) fills the workspace
