@@ -42,7 +42,7 @@ PEAK_FP32_TFLOPS = 157.3
 METRIC = "fwd+bwd attention TFLOP/s (bf16) and % of MI355X MFMA peak, 1 GPU"
 DEFAULT_WORKLOAD = "gqa_causal_8k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["bps_common.hpp", "lds_tile.hpp", "attn_kernels.hpp", "dkdv_gs.hpp", "attn_inst.hip"]
+KERNEL_SOURCES = ["bps_common.hpp", "lds_tile.hpp", "attn_kernels.hpp", "dkdv_gs.hpp", "fwd_pp.hpp", "attn_inst.hip"]
 
 
 # ------------------------------------------------------------------ counting
@@ -342,7 +342,7 @@ def ingest_counters(d, workload):
         out = {}
         with open(os.path.join(d, f"{tag}_counter_collection.csv")) as f:
             for r in csv.DictReader(f):
-                m = re.search(r"(attn_[a-z_]+?)(?:_ws)?_kernel", r["Kernel_Name"])
+                m = re.search(r"(attn_[a-z_]+?)(?:_ws|_gs)?_kernel", r["Kernel_Name"])
                 name = m.group(1) if m else ("copy" if "copy" in r["Kernel_Name"] else None)
                 if name:
                     out.setdefault(name, []).append(float(r["Counter_Value"]))
@@ -351,11 +351,15 @@ def ingest_counters(d, workload):
     copy_bytes = 1 << 30
     cf, cw = per_kernel("copyC")["copy"], per_kernel("copyD")["copy"]
     fetch_factor, write_factor = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    rec = {"_comment": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
-                       "each scaled by what it read for a 1 GiB device copy; source_hash is "
-                       "kernel_source_hash() of the sources the counters were taken on",
-           "calibration": {"copy_bytes": copy_bytes, "fetch_kib_read": round(cf), "write_kib_read": round(cw),
-                           "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)}}
+    rec = {}
+    if os.path.exists(TRAFFIC_FILE):   # records of other workloads are kept
+        with open(TRAFFIC_FILE) as f:
+            rec = {k: v for k, v in json.load(f).items() if not k.endswith(":" + workload)}
+    rec.update({"_comment": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
+                            "each scaled by what it read for a 1 GiB device copy; source_hash is "
+                            "kernel_source_hash() of the sources the counters were taken on",
+                "calibration": {"copy_bytes": copy_bytes, "fetch_kib_read": round(cf), "write_kib_read": round(cw),
+                                "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)}})
     fetch, write = per_kernel("C"), per_kernel("D")
     h = kernel_source_hash()
     for k in sorted(fetch):
@@ -364,6 +368,7 @@ def ingest_counters(d, workload):
         fb, wb = fetch[k] * 1024 * fetch_factor, write[k] * 1024 * write_factor
         rec[f"{k}:{workload}"] = {"source_hash": h, "fetch_bytes": int(fb), "write_bytes": int(wb),
                                   "bytes_per_launch": int(fb + wb)}
+    rec = {"_comment": rec.pop("_comment"), "calibration": rec.pop("calibration"), **dict(sorted(rec.items()))}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")

@@ -1730,6 +1730,7 @@ __global__ void __launch_bounds__(2 * DQK) attn_bwd_dq_reduce_kernel(BwdArgs a) 
 }  // namespace bps
 
 #include "dkdv_gs.hpp"
+#include "fwd_pp.hpp"
 
 namespace bps {
 
@@ -1753,6 +1754,14 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   if (nblocks <= 0) return hipSuccess;
   if constexpr (VM == 0 && FwdCfg<T, DQK, DV, 8>::WIDE_OK) {
     if ((a.s.Hq / a.s.Hkv) % 2 == 0) {   // head pairs of a GQA group
+      if constexpr (sizeof(T) == 2 && FwdPpCfg<DQK, DV>::ENABLED) {
+        if (fwd_pp_offsets_fit(a, DQK, DV)) {   // the two heads half a step apart
+          using CP = FwdPpCfg<DQK, DV>;
+          const long long nbp = (long long)a.s.B * (a.s.Hq / 2) * ((a.s.Sq + CP::BM - 1) / CP::BM);
+          hipLaunchKernelGGL((attn_fwd_pp_kernel<DQK, DV>), dim3((unsigned)nbp), dim3(CP::THREADS), 0, st, a);
+          return hipGetLastError();
+        }
+      }
       using C8 = FwdCfg<T, DQK, DV, 8, 2>;
       const long long nb8 = (long long)a.s.B * (a.s.Hq / 2) * ((a.s.Sq + C8::BM - 1) / C8::BM);
       hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, 0, 8, 2>), dim3((unsigned)nb8), dim3(C8::THREADS), 0, st, a);

@@ -54,6 +54,10 @@ def _run_oracle(case, var, heads=None):
 # Delta_i is off by up to u * sum_d |dO_id O_id|, and dx_ij = P_ij (dP_ij -
 # Delta_i) dS/dx inherits P_ij times that (dS/dx <= 1).  dQ, dK and dV
 # average this over many pairs; dbias shows it element by element.
+# u is the unit roundoff of round-to-nearest, half the spacing of the format
+# at 1: bf16 keeps 8 significant bits (spacing 2^-7 in [1, 2), so 2^-8), fp32
+# keeps 24 (2^-24).  The forward's own error in O (P rounded to bf16 before
+# the P V product) is left to the base tolerance.
 U_OUT = {"bf16": 2.0 ** -8, "fp32": 2.0 ** -24}
 
 
