@@ -39,44 +39,6 @@
 
 namespace bps {
 
-// Key tiles a query tile visits: [lo, hi) in tokens, per route.
-__device__ inline void kv_range(int route, bool causal, int Skv, int q0, int nq, const TileSum& qs, int& lo,
-                                int& hi) {
-  lo = 0;
-  hi = Skv;
-  if (route == kRouteDense) {
-    if (causal) hi = min(hi, q0 + nq);
-  } else if (route == kRouteFast) {
-    if (qs.cnt == 0) {
-      hi = 0;
-    } else {
-      lo = qs.smin;
-      hi = min(hi, qs.emax);
-      if (causal) hi = min(hi, q0 + nq);
-    }
-  }
-  if (hi < lo) hi = lo;
-}
-
-// Query tiles a key tile is visited by: [lo, hi) in tokens, per route.
-__device__ inline void q_range(int route, bool causal, int Sq, int k0, int nk, const TileSum& ks, int& lo,
-                               int& hi) {
-  lo = 0;
-  hi = Sq;
-  if (route == kRouteDense) {
-    if (causal) lo = k0;
-  } else if (route == kRouteFast) {
-    if (ks.cnt == 0) {
-      hi = 0;
-    } else {
-      lo = ks.smin;
-      hi = min(hi, ks.emax);
-      if (causal) lo = max(lo, k0);
-    }
-  }
-  if (hi < lo) hi = lo;
-}
-
 // Tile classes of a workgroup's walk, kept in LDS.  On the metadata routes
 // classifying a tile reads the 32-token summaries from global memory, a
 // round trip the loop would otherwise wait for on every step; instead the
@@ -309,7 +271,7 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(Fwd
   L /= n_qt;
   const int hkv = L % s.Hkv;
   const int b = L / s.Hkv;
-  const int qt = causal ? (n_qt - 1 - qrank) : qrank;
+  const int qt = BM == 128 ? q_tile_of(a.seg, b, qrank, n_qt, causal) : (causal ? n_qt - 1 - qrank : qrank);
   const int q0 = qt * BM;
 
   const int tid = threadIdx.x;
@@ -647,7 +609,7 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqC
   L /= n_qt;
   const int hkv = L % s.Hkv;
   const int b = L / s.Hkv;
-  const int qt = causal ? (n_qt - 1 - qrank) : qrank;
+  const int qt = BM == 128 ? q_tile_of(a.seg, b, qrank, n_qt, causal) : (causal ? n_qt - 1 - qrank : qrank);
   const int q0 = qt * BM;
 
   const int tid = threadIdx.x;
@@ -857,7 +819,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkvCfg
   L /= n_kt;
   const int hkv = L % s.Hkv;
   const int b = L / s.Hkv;
-  const int kt = krank;      // causal: low key tiles are the heaviest and come first
+  const int kt = k_tile_of(a.seg, b, krank, n_kt);   // fixed order: low key tiles (the longest causal walks) first
   const int k0 = kt * BN;
 
   const int tid = threadIdx.x;
@@ -1199,10 +1161,15 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
   int L = logical_block(nblocks, s.reverse);
   const int split = L % nsplit;
   L /= nsplit;
-  const int krank = L % n_kt;
+  const int rank = L % n_kt;
   L /= n_kt;
   const int hkv = L % s.Hkv;
   const int b = L / s.Hkv;
+  // The key tile.  Only the split instance takes the longest-walk-first
+  // order: the unsplit one keeps the fixed order, whose tile index the
+  // compiler recomputes from the block index instead of holding it (a loaded
+  // index costs it SGPR spill reloads, measured 3 % slower on packed 8K).
+  const int krank = SPLIT ? k_tile_of(a.seg, b, rank, n_kt) : rank;
   const int k0 = krank * BN;
 
   const int tid = threadIdx.x;

@@ -98,6 +98,14 @@ struct SegMetaArgs {
   int* route;             // [B]
 };
 
+// Longest-walk-first tile orders of every batch row (qord, kord in seg).
+struct TileOrderArgs {
+  int B, Sq, Skv, causal;
+  SegView seg;
+  int* qord;   // [B, ceil(Sq / 128)]
+  int* kord;   // [B, ceil(Skv / 128)]
+};
+
 struct MaskArgs {
   int B, Sq, Skv, causal, has_meta;
   SegView seg;
@@ -147,6 +155,8 @@ hipError_t launch_ring_reduce(int dtype_bf16, const RingReduceArgs& a, hipStream
 // result of hipGetLastError() after its launches.
 hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st);
 hipError_t launch_debug_mask(const MaskArgs& a, hipStream_t st);
+// Longest-walk-first tile orders (after launch_seg_meta on the same stream).
+hipError_t launch_tile_order(const TileOrderArgs& a, hipStream_t st);
 // out[b] = route[b] for b < B (route NULL: kRouteDense everywhere).
 hipError_t launch_route_rows(const int* route, int B, int* out, hipStream_t st);
 

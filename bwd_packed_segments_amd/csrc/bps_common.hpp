@@ -138,7 +138,23 @@ struct SegView {
   const ChunkSum* sum_kv;  // [B, nch_kv]
   const int* route;      // [B] 1 fast, 2 general
   int nch_q, nch_kv;
+  // Per batch row, the order in which workgroups take tiles, longest walk
+  // first: query tiles of 128 (forward and dQ) and key tiles of 128 (dK/dV).
+  // NULL: the fixed order (causal: the tiles with the longest causal walks
+  // first).
+  const int* qord;       // [B, ceil(Sq / 128)]
+  const int* kord;       // [B, ceil(Skv / 128)]
 };
+
+// Query tile of 128 that the workgroup of rank r in batch row b takes.
+__device__ inline int q_tile_of(const SegView& sv, int b, int r, int n_qt, bool causal) {
+  if (sv.qord) return sv.qord[(size_t)b * n_qt + r];
+  return causal ? n_qt - 1 - r : r;
+}
+// Key tile of 128 that the workgroup of rank r in batch row b takes.
+__device__ inline int k_tile_of(const SegView& sv, int b, int r, int n_kt) {
+  return sv.kord ? sv.kord[(size_t)b * n_kt + r] : r;
+}
 
 enum { kRouteDense = 0, kRouteFast = 1, kRouteGeneral = 2 };
 enum { kTileSkip = 0, kTileFull = 1, kTilePart = 2 };
@@ -190,6 +206,44 @@ __device__ inline int classify_tile(int route, bool causal, int Skv, int r0, int
       qs.idmin == ks.idmin && (!causal || ks.posmax <= qs.posmin))
     return kTileFull;
   return kTilePart;
+}
+
+// Key tiles a query tile visits: [lo, hi) in tokens, per route.
+__device__ inline void kv_range(int route, bool causal, int Skv, int q0, int nq, const TileSum& qs, int& lo,
+                                int& hi) {
+  lo = 0;
+  hi = Skv;
+  if (route == kRouteDense) {
+    if (causal) hi = min(hi, q0 + nq);
+  } else if (route == kRouteFast) {
+    if (qs.cnt == 0) {
+      hi = 0;
+    } else {
+      lo = qs.smin;
+      hi = min(hi, qs.emax);
+      if (causal) hi = min(hi, q0 + nq);
+    }
+  }
+  if (hi < lo) hi = lo;
+}
+
+// Query tiles a key tile is visited by: [lo, hi) in tokens, per route.
+__device__ inline void q_range(int route, bool causal, int Sq, int k0, int nk, const TileSum& ks, int& lo,
+                               int& hi) {
+  lo = 0;
+  hi = Sq;
+  if (route == kRouteDense) {
+    if (causal) lo = k0;
+  } else if (route == kRouteFast) {
+    if (ks.cnt == 0) {
+      hi = 0;
+    } else {
+      lo = ks.smin;
+      hi = min(hi, ks.emax);
+      if (causal) lo = max(lo, k0);
+    }
+  }
+  if (hi < lo) hi = lo;
 }
 
 // Per-token metadata used by the element mask: (run start, run end) on the

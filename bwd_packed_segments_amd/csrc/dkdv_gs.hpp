@@ -55,32 +55,6 @@ struct DkvGsCfg {
   static constexpr bool ENABLED = (DQK == 64 || DQK == 128) && (DV == 64 || DV == 128) && LDS_BYTES <= 160 * 1024;
 };
 
-// Raw buffer resource over a byte range starting at p (gfx9 format word 3).
-__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, -1, 0x00020000);
-}
-
-// Direct-to-LDS loads written as inline assembly.  Each lane's data lands
-// at the wave's LDS base (M0) + lane * size.  The compiler does not see
-// these as LDS writes, so it does not wait for them before every LDS read
-// that follows (its alias analysis cannot tell the phase buffers apart);
-// the kernel waits for them itself (vmcnt) before the barrier that
-// publishes a buffer.  They write no registers.
-// lds and soff must be wave-uniform (they are moved to scalar registers).
-__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r),
-                 "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "memory");
-}
-__device__ inline void lds_load4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g)
-               : "memory");
-}
-
 // Byte offset of this lane's natural operand fragment t (row n, elements
 // 16 t + 8 hf) in a [32 x D] bf16 tile.
 template <int D>
@@ -116,11 +90,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
   const int g = s.Hq / s.Hkv;
   const int nblocks = s.B * s.Hkv * n_kt;
   int L = logical_block(nblocks, s.reverse);
-  const int krank = L % n_kt;
+  const int rank = L % n_kt;
   L /= n_kt;
   const int hkv = L % s.Hkv;
   const int b = L / s.Hkv;
-  const int k0 = krank * BN;
+  const int k0 = k_tile_of(a.seg, b, rank, n_kt) * BN;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;

@@ -59,16 +59,6 @@ inline bool fwd_pp_offsets_fit(const FwdArgs& a, int dqk, int dv) {
   return a.sk.t >= 0 && a.sv.t >= 0 && k < lim && v < lim;
 }
 
-// A workgroup-uniform pointer, held in scalar registers (the buffer
-// resource of a scalar-operand load must be).
-template <typename P>
-__device__ inline const P* uniform_ptr(const P* p) {
-  const uint64_t x = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-  return reinterpret_cast<const P*>(((uint64_t)hi << 32) | lo);
-}
-
 template <int DQK, int DV>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
     attn_fwd_pp_kernel(FwdArgs a) {
@@ -93,7 +83,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
   L /= n_qt;
   const int hkv = L % s.Hkv;
   const int b = L / s.Hkv;
-  const int qt = causal ? (n_qt - 1 - qrank) : qrank;
+  const int qt = q_tile_of(a.seg, b, qrank, n_qt, causal);
   const int q0 = qt * BM;
 
   const int tid = threadIdx.x;

@@ -103,6 +103,42 @@ __device__ inline typename Elem<T>::F8 frag_tr(const T* tile, int x0, int y0, in
   }
 }
 
+// Raw buffer resource over a byte range starting at p (gfx9 format word 3).
+__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, -1, 0x00020000);
+}
+
+// Direct-to-LDS loads written as inline assembly.  Each lane's data lands
+// at the wave's LDS base (M0) + lane * size.  The compiler does not see
+// these as LDS writes, so it does not wait for them before every LDS read
+// that follows (its alias analysis cannot tell the phase buffers apart);
+// the kernel waits for them itself (vmcnt) before the barrier that
+// publishes a buffer.  They write no registers.
+// lds and soff must be wave-uniform (they are moved to scalar registers).
+__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+__device__ inline void lds_load4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g)
+               : "memory");
+}
+
+// A workgroup-uniform pointer, held in scalar registers (the buffer
+// resource of a scalar-operand load must be).
+template <typename P>
+__device__ inline const P* uniform_ptr(const P* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const P*>(((uint64_t)hi << 32) | lo);
+}
+
 // Fills a [ROWS x D] tile from global memory rows base + r * row_stride.
 template <typename T, int ROWS, int D, int THREADS>
 struct TileLoad {

@@ -217,6 +217,70 @@ __global__ __launch_bounds__(256) void debug_mask_kernel(MaskArgs a) {
   }
 }
 
+// Longest-walk-first tile orders for rows on the general route.  There
+// the walk of a tile (the key tiles a query tile visits, or the query tiles
+// a key tile is visited by) depends on where the segments fall, not on the
+// tile's position, and the fixed order can leave long walks for last.  One
+// workgroup per (batch row, side) counts the visited units of every tile of
+// 128 (key or query units of 64, classified from the 32-token summaries as
+// the attention kernels classify them) and ranks the tiles by that count,
+// longest first, ties by index.  Rows on the fast route keep the fixed
+// order (measured faster there: their walks follow the segment layout
+// closely and neighbouring tiles share K/V or Q/dO in L2).  The order only
+// changes which workgroup runs when; each tile's arithmetic is the same.
+constexpr int kOrdThreads = 1024;
+constexpr int kOrdTiles = 1024;   // tiles of 128 per row and side
+constexpr int kOrdUnits = 2048;   // walk units of 64 per row and side
+
+__global__ __launch_bounds__(kOrdThreads) void tile_order_kernel(TileOrderArgs t) {
+  __shared__ TileSum tsum[kOrdTiles];
+  __shared__ TileSum usum[kOrdUnits];
+  __shared__ int lo_u[kOrdTiles], hi_u[kOrdTiles], len[kOrdTiles];
+  const int b = blockIdx.x;
+  const bool qside = blockIdx.y == 0;   // query tiles over key units, else key tiles over query units
+  const int tid = threadIdx.x;
+  const bool causal = t.causal != 0;
+  const int route = t.seg.route[b];
+  const int n_t = ((qside ? t.Sq : t.Skv) + 127) / 128;
+  const int n_u = ((qside ? t.Skv : t.Sq) + 63) / 64;
+  int* ord = (qside ? t.qord : t.kord) + (size_t)b * n_t;
+  if (route != kRouteGeneral || n_t > kOrdTiles || n_u > kOrdUnits) {   // the fixed order
+    for (int r = tid; r < n_t; r += kOrdThreads) ord[r] = (qside && causal) ? n_t - 1 - r : r;
+    return;
+  }
+  const int nch_t = qside ? t.seg.nch_q : t.seg.nch_kv;
+  const int nch_u = qside ? t.seg.nch_kv : t.seg.nch_q;
+  const ChunkSum* row_t = (qside ? t.seg.sum_q : t.seg.sum_kv) + (size_t)b * nch_t;
+  const ChunkSum* row_u = (qside ? t.seg.sum_kv : t.seg.sum_q) + (size_t)b * nch_u;
+  for (int i = tid; i < n_t; i += kOrdThreads) {
+    const TileSum ts = tile_sum(row_t, nch_t, i * 128, 128);
+    int lo, hi;
+    if (qside) kv_range(route, causal, t.Skv, i * 128, 128, ts, lo, hi);
+    else q_range(route, causal, t.Sq, i * 128, 128, ts, lo, hi);
+    tsum[i] = ts;
+    lo_u[i] = lo / 64;
+    hi_u[i] = (hi + 63) / 64;
+    len[i] = 0;
+  }
+  for (int j = tid; j < n_u; j += kOrdThreads) usum[j] = tile_sum(row_u, nch_u, j * 64, 64);
+  __syncthreads();
+  // Every (tile, unit) pair in the tile's range, spread over all threads.
+  for (int p = tid; p < n_t * n_u; p += kOrdThreads) {
+    const int i = p / n_u, j = p - i * n_u;
+    if (j < lo_u[i] || j >= hi_u[i]) continue;
+    const int c = qside ? classify_tile(route, causal, t.Skv, i * 128, 128, j * 64, 64, tsum[i], usum[j])
+                        : classify_tile(route, causal, t.Skv, j * 64, 64, i * 128, 128, usum[j], tsum[i]);
+    if (c != kTileSkip) atomicAdd(&len[i], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < n_t; i += kOrdThreads) {
+    const int li = len[i];
+    int r = 0;
+    for (int u = 0; u < n_t; ++u) r += (len[u] > li) | ((len[u] == li) & (u < i));
+    ord[r] = i;
+  }
+}
+
 // The route each batch row took (route NULL: no metadata, every row dense).
 __global__ __launch_bounds__(256) void route_rows_kernel(const int* route, int B, int* out) {
   for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < B; b += gridDim.x * blockDim.x)
@@ -235,6 +299,12 @@ hipError_t launch_route_rows(const int* route, int B, int* out, hipStream_t st) 
 hipError_t launch_seg_meta(const SegMetaArgs& a, hipStream_t st) {
   dim3 grid(a.B, a.sides);
   hipLaunchKernelGGL(seg_meta_kernel, grid, dim3(kSegThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_order(const TileOrderArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(tile_order_kernel, dim3(a.B, 2), dim3(kOrdThreads), 0, st, a);
   return hipGetLastError();
 }
 
