@@ -342,7 +342,7 @@ def ingest_counters(d, workload):
         out = {}
         with open(os.path.join(d, f"{tag}_counter_collection.csv")) as f:
             for r in csv.DictReader(f):
-                m = re.search(r"(attn_[a-z_]+?)(?:_ws|_gs)?_kernel", r["Kernel_Name"])
+                m = re.search(r"(attn_[a-z_]+?)(?:_ws|_gs|_pp)?_kernel", r["Kernel_Name"])
                 name = m.group(1) if m else ("copy" if "copy" in r["Kernel_Name"] else None)
                 if name:
                     out.setdefault(name, []).append(float(r["Counter_Value"]))
