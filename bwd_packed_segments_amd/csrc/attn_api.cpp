@@ -119,6 +119,9 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p, boo
   if ((st = check_strides("q", d->q, vec)) != ATTN_OK) return st;
   if ((st = check_strides("k", d->k, vec)) != ATTN_OK) return st;
   if ((st = check_strides("v", d->v, vec)) != ATTN_OK) return st;
+  if (d->k.token > bps::kMaxKvTokenStride || d->v.token > bps::kMaxKvTokenStride)
+    return fail(ATTN_E_UNSUPPORTED, "k and v token strides must not exceed %lld elements (got %lld, %lld)",
+                (long long)bps::kMaxKvTokenStride, (long long)d->k.token, (long long)d->v.token);
   if ((st = check_strides("o", d->o, vec)) != ATTN_OK) return st;
   if ((st = check_disjoint("o (and dO)", d->o, d->B, d->Sq, d->Hq, d->Dv)) != ATTN_OK) return st;
   p->scale = d->scale == 0.f ? 1.f / std::sqrt(static_cast<float>(d->Dqk)) : d->scale;

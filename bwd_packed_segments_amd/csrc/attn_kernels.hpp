@@ -34,6 +34,8 @@
 // Features, mask-free KV padding).
 #pragma once
 
+#include <type_traits>
+
 #include "bps_args.hpp"
 #include "lds_tile.hpp"
 
@@ -622,8 +624,8 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqC
 
   const T* qp = static_cast<const T*>(a.q) + b * a.sq.b + h * a.sq.h;
   const T* dop = static_cast<const T*>(a.dout) + b * a.so.b + h * a.so.h;
-  const T* kp = static_cast<const T*>(a.k) + b * a.sk.b + hkv * a.sk.h;
-  const T* vp = static_cast<const T*>(a.v) + b * a.sv.b + hkv * a.sv.h;
+  const T* kp = uniform_ptr(static_cast<const T*>(a.k) + b * a.sk.b + hkv * a.sk.h);
+  const T* vp = uniform_ptr(static_cast<const T*>(a.v) + b * a.sv.b + hkv * a.sv.h);
 
   F8 qf[DQK / 16];
   F8 dof[DV / 16];
@@ -677,11 +679,11 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqC
     const int k0 = kt * BN;
     const int nvalid = min(BN, s.Skv - k0);
     if (nvalid == BN) {
-      TileLoad<T, BN, DQK, C::THREADS>::direct(kp + k0 * a.sk.t, a.sk.t, Ks, tid);
-      TileLoad<T, BN, DV, C::THREADS>::direct(vp + k0 * a.sv.t, a.sv.t, Vs, tid);
+      TileLoad<T, BN, DQK, C::THREADS, true>::direct(kp + k0 * a.sk.t, a.sk.t, Ks, tid);
+      TileLoad<T, BN, DV, C::THREADS, true>::direct(vp + k0 * a.sv.t, a.sv.t, Vs, tid);
     } else {
-      TileLoad<T, BN, DQK, C::THREADS>::staged(kp + k0 * a.sk.t, a.sk.t, nvalid, Ks, tid);
-      TileLoad<T, BN, DV, C::THREADS>::staged(vp + k0 * a.sv.t, a.sv.t, nvalid, Vs, tid);
+      TileLoad<T, BN, DQK, C::THREADS, true>::staged(kp + k0 * a.sk.t, a.sk.t, nvalid, Ks, tid);
+      TileLoad<T, BN, DV, C::THREADS, true>::staged(vp + k0 * a.sv.t, a.sv.t, nvalid, Vs, tid);
     }
     if (general) stage_kv_meta<BN>(a.seg, b, s.Skv, k0, kid, tid, nvalid == BN);
   };
@@ -696,20 +698,73 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqC
 #pragma unroll
   for (int d = 0; d < DQK / 32; ++d) dqa[d] = f32x16{};
 
+  // Per-lane LDS byte offsets inside a stage, fixed for the walk (bf16): K
+  // rows and V rows (fragment t of row n of the first 32-key block) and the
+  // transposed K reads (column block d, rows y and y + 8 of the first
+  // 16-row group).  The key block and the stage add immediates: the loop is
+  // unrolled over the two stages.
+  uint32_t kro[DQK / 16], vro[DV / 16], ktr[DQK / 32][2];
+  if constexpr (sizeof(T) == 2) {
+    using FK = TileFmt<T, DQK>;
+    using FV = TileFmt<T, DV>;
+#pragma unroll
+    for (int t = 0; t < DQK / 16; ++t) kro[t] = (uint32_t)FK::off(n, 16 * t + 8 * hf) * 2;
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t) vro[t] = (uint32_t)(BN * DQK * 2 + FV::off(n, 16 * t + 8 * hf) * 2);
+#pragma unroll
+    for (int d = 0; d < DQK / 32; ++d)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int G = lane >> 4, i = lane & 15;
+        ktr[d][p] = (uint32_t)FK::off(4 * (G >> 1) + (i >> 2) + 8 * p, 32 * d + 16 * (G & 1) + 4 * (i & 3)) * 2;
+      }
+  }
+  // Natural operand fragment t of row blk * 32 + n of the K (V) tile in
+  // stage ST; transposed K fragment (column block d, rows y0 ..).
+  auto rd_k = [&](auto stc, int blk, int t) __attribute__((always_inline)) -> F8 {
+    constexpr int ST = decltype(stc)::value;
+    const T* Ks = reinterpret_cast<const T*>(stage(ST));
+    if constexpr (sizeof(T) == 2)
+      return *reinterpret_cast<const F8*>(smem + ST * C::STAGE_BYTES + blk * 32 * DQK * 2 + kro[t]);
+    else
+      return frag_row<T, DQK>(Ks, blk * 32 + n, 16 * t + 8 * hf);
+  };
+  auto rd_v = [&](auto stc, int blk, int t) __attribute__((always_inline)) -> F8 {
+    constexpr int ST = decltype(stc)::value;
+    const T* Vs = reinterpret_cast<const T*>(stage(ST)) + BN * DQK;
+    if constexpr (sizeof(T) == 2)
+      return *reinterpret_cast<const F8*>(smem + ST * C::STAGE_BYTES + blk * 32 * DV * 2 + vro[t]);
+    else
+      return frag_row<T, DV>(Vs, blk * 32 + n, 16 * t + 8 * hf);
+  };
+  auto rd_ktr = [&](auto stc, int d, int y0) __attribute__((always_inline)) -> F8 {
+    constexpr int ST = decltype(stc)::value;
+    const T* Ks = reinterpret_cast<const T*>(stage(ST));
+    if constexpr (sizeof(T) == 2) {
+      const char* base = smem + ST * C::STAGE_BYTES + y0 * DQK * 2;
+      const bf16x4v x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BPS_LDS bf16x4v*)(base + ktr[d][0]));
+      const bf16x4v y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BPS_LDS bf16x4v*)(base + ktr[d][1]));
+      return F8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    } else {
+      return frag_tr<T, DQK>(Ks, d * 32, y0, lane);
+    }
+  };
+
   int cls;
   int kt = next_tile(t_lo, cls);
-  int buf = 0;
   if (kt < t_hi) issue(kt, 0);
   wait_vm();
   __syncthreads();
 
-  while (kt < t_hi) {
+  // One key tile in stage ST (the next one fetched into the other stage).
+  auto step = [&](auto stc) __attribute__((always_inline)) -> bool {
+    constexpr int ST = decltype(stc)::value;
+    if (kt >= t_hi) return false;
     int ncls;
     const int nkt = next_tile(kt + 1, ncls);
-    if (C::NBUF == 2 && nkt < t_hi) issue(nkt, buf ^ 1);
+    if (C::NBUF == 2 && nkt < t_hi) issue(nkt, ST ^ 1);
 
-    const T* Ks = reinterpret_cast<const T*>(stage(buf));
-    const T* Vs = Ks + BN * DQK;
+    const T* Vs = reinterpret_cast<const T*>(stage(ST)) + BN * DQK;
     const int* kid = reinterpret_cast<const int*>(Vs + BN * DV);
     const int k0 = kt * BN;
 
@@ -718,9 +773,9 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqC
       // S^T and dP^T for 32 keys x this wave's 32 queries.
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int t = 0; t < DQK / 16; ++t) sacc = mma(frag_row<T, DQK>(Ks, blk * 32 + n, 16 * t + 8 * hf), qf[t], sacc);
+      for (int t = 0; t < DQK / 16; ++t) sacc = mma(rd_k(stc, blk, t), qf[t], sacc);
 #pragma unroll
-      for (int t = 0; t < DV / 16; ++t) pacc = mma(frag_row<T, DV>(Vs, blk * 32 + n, 16 * t + 8 * hf), dof[t], pacc);
+      for (int t = 0; t < DV / 16; ++t) pacc = mma(rd_v(stc, blk, t), dof[t], pacc);
       if constexpr (VAR) {
         // Variant logits, masked to -inf, then P and dLoss/dx = P (dP -
         // Delta) dS/dx in one pass.
@@ -751,20 +806,26 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DqC
       for (int s2 = 0; s2 < 2; ++s2) {
         const F8 dsf = E::cvt8(slots8(sacc, s2));
 #pragma unroll
-        for (int d = 0; d < DQK / 32; ++d)
-          dqa[d] = mma(frag_tr<T, DQK>(Ks, d * 32, blk * 32 + 16 * s2, lane), dsf, dqa[d]);
+        for (int d = 0; d < DQK / 32; ++d) dqa[d] = mma(rd_ktr(stc, d, blk * 32 + 16 * s2), dsf, dqa[d]);
       }
     }
 
     if (C::NBUF == 1) {
       __syncthreads();
-      if (nkt < t_hi) issue(nkt, buf);
+      if (nkt < t_hi) issue(nkt, ST);
     }
     wait_vm();
     __syncthreads();
-    if (C::NBUF == 2) buf ^= 1;
     kt = nkt;
     cls = ncls;
+    return true;
+  };
+  if constexpr (C::NBUF == 2) {
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+    }
+  } else {
+    while (step(std::integral_constant<int, 0>{})) {
+    }
   }
 
   if (qi < s.Sq) {

@@ -113,6 +113,10 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr int kChunk = 32;   // tokens per metadata summary
 
+// Largest token stride (elements) of k and v: the dQ kernel addresses its
+// key/value tile rows with 32-bit offsets.
+constexpr int64_t kMaxKvTokenStride = (int64_t)1 << 24;
+
 // Summary of kChunk consecutive tokens of one batch row, over the tokens
 // that carry a nonzero segment id (cnt of them).  s/e are the bounds
 // [start, end) of the contiguous id run holding each token.

@@ -140,7 +140,10 @@ __device__ inline const P* uniform_ptr(const P* p) {
 }
 
 // Fills a [ROWS x D] tile from global memory rows base + r * row_stride.
-template <typename T, int ROWS, int D, int THREADS>
+// OFF32: lane offsets in 32-bit arithmetic (the caller guarantees
+// ROWS * row_stride < 2^31 elements); a kernel short of registers keeps one
+// register per load instead of a pair.
+template <typename T, int ROWS, int D, int THREADS, bool OFF32 = false>
 struct TileLoad {
   using F = TileFmt<T, D>;
   using E = Elem<T>;
@@ -156,7 +159,8 @@ struct TileLoad {
       const int s = x * THREADS + tid;
       const int r = s / F::NC;
       const int c = F::swz(r, s % F::NC);
-      const T* g = base + r * row_stride + c * F::EPC;
+      const T* g = OFF32 ? base + ((uint32_t)r * (uint32_t)row_stride + (uint32_t)(c * F::EPC))
+                         : base + r * row_stride + c * F::EPC;
       T* wave_base = tile + (x * THREADS + (tid & ~63)) * F::EPC;
       __builtin_amdgcn_global_load_lds(g, (BPS_LDS void*)wave_base, 16, 0, 0);
     }
@@ -170,7 +174,9 @@ struct TileLoad {
       const int r = s / F::NC;
       const int c = F::swz(r, s % F::NC);
       u32x4v v = u32x4v{0u, 0u, 0u, 0u};
-      if (r < nvalid) v = *reinterpret_cast<const u32x4v*>(base + r * row_stride + c * F::EPC);
+      if (r < nvalid)
+        v = *reinterpret_cast<const u32x4v*>(OFF32 ? base + ((uint32_t)r * (uint32_t)row_stride + (uint32_t)(c * F::EPC))
+                                                   : base + r * row_stride + c * F::EPC);
       *reinterpret_cast<u32x4v*>(tile + s * F::EPC) = v;
     }
   }
