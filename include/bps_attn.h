@@ -52,8 +52,11 @@
  * stride spanning the whole packed row (TransformerEngine PR 2358, review of
  * the KV-packed stride).  Strides the library writes through (O, and for
  * the backward Q, K, V, which dQ, dK, dV share) must not overlap, i.e. no
- * two elements at one address: otherwise ATTN_E_UNSUPPORTED.  LSE is [B, Hq, Sq] fp32, contiguous.  Segment
- * metadata are int32 [B, S], contiguous.
+ * two elements at one address: otherwise ATTN_E_UNSUPPORTED.  The token
+ * strides of K and V may not exceed 2^24 elements (the kernels address key
+ * tile rows with 32-bit offsets): otherwise ATTN_E_UNSUPPORTED.  LSE is
+ * [B, Hq, Sq] fp32, contiguous.  Segment metadata are int32 [B, S],
+ * contiguous.
  *
  * Memory and streams.  Every pointer argument except route_out is device
  * memory owned by the caller; the library allocates nothing and keeps no

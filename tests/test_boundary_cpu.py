@@ -299,6 +299,21 @@ def test_overlapping_output_strides_rejected():
     assert st == B.ATTN_E_WORKSPACE, text
 
 
+def test_kv_token_stride_limit():
+    """K and V token strides above 2^24 elements are rejected before any
+    HIP call (the kernels address key tile rows with 32-bit offsets); the
+    limit itself passes on to the workspace check."""
+    big = (1 << 24) + 128
+    for which in ("k", "v"):
+        d = good(B=1, **{which: (300 * big, big, 128)})
+        st, text = B.validate_fwd(d)
+        assert st == B.ATTN_E_UNSUPPORTED and "token strides" in text, text
+    lim = 1 << 24
+    d = good(B=1, k=(300 * lim, lim, 128), v=(300 * lim, lim, 128))
+    st, text = B.validate_bwd(d)
+    assert st == B.ATTN_E_WORKSPACE, text
+
+
 def test_disjoint_packed_views_pass_the_stride_check():
     """Packed QKV [B, S, 3, H, D] and KV [B, S, 2, Hkv, D] views are disjoint
     per tensor: validation passes the stride checks and stops at the missing
