@@ -11,6 +11,7 @@ call does, and it raises if the library is missing.
 from .binding import (  # noqa: F401
     ATTN_FORCE_GENERAL,
     ATTN_FUSED_BWD,
+    ATTN_LOG_ROUTE,
     ATTN_REVERSE_SCHEDULE,
     ATTN_BWD_ALL,
     ATTN_BWD_DKDV,

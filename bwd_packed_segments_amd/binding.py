@@ -20,6 +20,7 @@ ATTN_BF16, ATTN_FP32 = 0, 1
 ATTN_FORCE_GENERAL = 1 << 0
 ATTN_REVERSE_SCHEDULE = 1 << 1
 ATTN_FUSED_BWD = 1 << 2
+ATTN_LOG_ROUTE = 1 << 3
 ROUTE_NAMES = {0: "dense", 1: "fast", 2: "general"}
 
 STATUS_NAMES = {

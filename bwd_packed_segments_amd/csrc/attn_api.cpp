@@ -106,7 +106,7 @@ attn_status make_plan(const attn_desc* d, const attn_segments* seg, Plan* p, boo
     return fail(ATTN_E_UNSUPPORTED, "head dims (Dqk=%d, Dv=%d) not built for dtype %d", d->Dqk, d->Dv, d->dtype);
   if (d->causal != 0 && d->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
   if (!std::isfinite(d->scale) || d->scale < 0.f) return fail(ATTN_E_INVALID, "scale must be finite and >= 0");
-  if (d->flags & ~static_cast<uint32_t>(ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE | ATTN_FUSED_BWD))
+  if (d->flags & ~static_cast<uint32_t>(ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE | ATTN_FUSED_BWD | ATTN_LOG_ROUTE))
     return fail(ATTN_E_INVALID, "unknown flag bits 0x%x", d->flags);
   p->fused = (d->flags & ATTN_FUSED_BWD) != 0;
   if (p->fused && (d->dtype != ATTN_BF16 || d->Dqk > 128 || d->Dv > 128))
@@ -353,6 +353,31 @@ hipError_t dispatch_bwd(int phases, int dtype, int dqk, int dv, bool var_delta, 
 int route_of(const Plan& p) {
   if (!p.meta) return ATTN_ROUTE_DENSE;
   return p.fast_candidate ? ATTN_ROUTE_FAST : ATTN_ROUTE_GENERAL;
+}
+
+// ATTN_LOG_ROUTE: after the metadata preparation of `call`, wait for the
+// stream and report on stderr every batch row that the device moved from the
+// requested fast route to the general route (debug only: it synchronises).
+attn_status log_route(const attn_desc* d, const Plan& p, const char* ws, hipStream_t hs, const char* call) {
+  if (!(d->flags & ATTN_LOG_ROUTE) || !p.meta || !p.fast_candidate || d->B == 0) return ATTN_OK;
+  hipError_t e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return fail(ATTN_E_DEVICE, "route log: %s", hipGetErrorString(e));
+  int32_t rows[256];
+  const int32_t* src = reinterpret_cast<const int32_t*>(ws + p.off_route);
+  int moved = 0;
+  for (int b0 = 0; b0 < d->B; b0 += 256) {
+    const int nb = std::min(256, d->B - b0);
+    e = hipMemcpy(rows, src + b0, nb * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "route log: %s", hipGetErrorString(e));
+    for (int i = 0; i < nb; ++i) {
+      if (rows[i] == ATTN_ROUTE_FAST) continue;
+      ++moved;
+      std::fprintf(stderr, "bps_attn: %s: batch row %d takes the general route (fast route requested; the "
+                   "device check of Q and KV metadata failed)\n", call, b0 + i);
+    }
+  }
+  if (moved) std::fprintf(stderr, "bps_attn: %s: %d of %d batch rows on the general route\n", call, moved, d->B);
+  return ATTN_OK;
 }
 
 attn_status check_ws(void* ws, size_t have, size_t need) {
@@ -623,6 +648,7 @@ attn_status fwd_impl(const attn_desc* d, const attn_segments* seg, const attn_va
     a.var = var_view(d, var, vp, ws, false);
     if (d->Sq > 0) {
       if ((st = prepare_segments(d, seg, p, ws, hs, &a.seg)) != ATTN_OK) return st;
+      if ((st = log_route(d, p, ws, hs, "forward")) != ATTN_OK) return st;
       const int vm = !vp.on ? 0 : (var->bias != nullptr || var->softcap > 0.f) ? 2 : 1;
       hipError_t e = dispatch_fwd(d->dtype, d->Dqk, d->Dv, vm, a, hs);
       if (e != hipSuccess) return fail(ATTN_E_DEVICE, "forward launch: %s", hipGetErrorString(e));
@@ -705,6 +731,7 @@ attn_status bwd_impl(int32_t phases, const attn_desc* d, const attn_segments* se
     }
     if (!(d->Sq == 0 && d->Skv == 0)) {
       if ((st = prepare_segments(d, seg, p, ws, hs, &a.seg, prep)) != ATTN_OK) return st;
+      if (prep && (st = log_route(d, p, ws, hs, "backward")) != ATTN_OK) return st;
       const bool var_attn = vp.on && (var->bias != nullptr || var->softcap > 0.f);
       const bool var_delta = vp.on && var->dsink != nullptr;
       e = dispatch_bwd(phases, d->dtype, d->Dqk, d->Dv, var_delta, var_attn, a, hs);

@@ -100,8 +100,19 @@ enum {
   ATTN_FORCE_GENERAL = 1u << 0,     /* never take the fast route (tests, ring steps) */
   ATTN_REVERSE_SCHEDULE = 1u << 1,  /* visit workgroup tiles in reverse order (tests:
                                        results must not depend on schedule) */
-  ATTN_FUSED_BWD = 1u << 2          /* backward: single-pass form (see below) */
+  ATTN_FUSED_BWD = 1u << 2,         /* backward: single-pass form (see below) */
+  ATTN_LOG_ROUTE = 1u << 3          /* debug: report fast-route downgrades on stderr
+                                       (synchronises; see below) */
 };
+
+/* ATTN_LOG_ROUTE: the TransformerEngine page on fused attention sharding
+ * (PR 3516, review) asks for a warning when the fast path is not taken.
+ * With this flag, a call that prepares segment metadata (attn_fwd and its
+ * variants, and the backward's prepare phase) waits for its stream, reads
+ * the route every batch row took and writes one line to stderr per row the
+ * device moved from the requested fast route to the general route.  It
+ * synchronises the stream, so it is for debugging; attn_route_rows gives
+ * the same information without a synchronisation. */
 
 /* ATTN_FUSED_BWD: the single-pass backward of the maxdiffusion page on custom
  * splash and ring attention (Key Features: one kernel over key blocks, query
@@ -146,7 +157,7 @@ typedef struct {
   int32_t causal;                   /* 0 or 1 */
   float scale;                      /* softmax scale; 0 selects 1/sqrt(Dqk) */
   uint32_t flags;                   /* ATTN_FORCE_GENERAL | ATTN_REVERSE_SCHEDULE |
-                                       ATTN_FUSED_BWD */
+                                       ATTN_FUSED_BWD | ATTN_LOG_ROUTE */
   attn_strides q, k, v, o;          /* layouts of Q, K, V, O (and dQ, dK, dV, dO) */
 } attn_desc;
 
@@ -160,7 +171,11 @@ typedef struct {
 
 /* Workspace bytes needed by attn_fwd / attn_bwd for this descriptor and
  * metadata (seg may be NULL).  Returns 0 for an invalid descriptor (the
- * matching call then reports why). */
+ * matching call then reports why).  As in the TransformerEngine page that
+ * moves every layout onto the non-packed attention calls (PR 2358, Greptile
+ * Overview: one workspace-size computation for all layouts), the size
+ * depends only on the shapes, dtype, flags and which metadata are given,
+ * never on the layout strides, and the caller allocates it. */
 size_t attn_fwd_workspace_size(const attn_desc* desc, const attn_segments* seg);
 size_t attn_bwd_workspace_size(const attn_desc* desc, const attn_segments* seg);
 
@@ -368,7 +383,12 @@ attn_status attn_bwd_ex_phase(int32_t phases, const attn_desc* desc, const attn_
                               void* workspace, size_t workspace_bytes,
                               void* stream, int32_t* route_out);
 
-/* Text of the last non-OK status returned on this thread ("" if none). */
+/* Text of the last non-OK status returned on this thread ("" if none).  The
+ * JAX batcher page (PR 2692, Description) shows the failure this replaces: a
+ * segment-id / segment-position shape mismatch surfacing as an assertion
+ * deep inside the primitive.  Here every argument is checked on the host
+ * before any launch, and the message names the argument and the rule it
+ * broke. */
 const char* attn_last_error(void);
 
 /* Library version string. */

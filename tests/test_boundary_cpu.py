@@ -255,7 +255,7 @@ def test_fused_bwd_validation_and_workspace():
     assert B.ex_workspace_sizes(good(flags=F), _var(sink=ptr))[1] == B.bwd_workspace_size(good(flags=F))
     st, text = B.validate_ring_fwd(good(flags=F), None, 2)
     assert st == B.ATTN_E_UNSUPPORTED and "ring" in text
-    st, text = B.validate_bwd(good(flags=1 << 3))
+    st, text = B.validate_bwd(good(flags=1 << 4))
     assert st == B.ATTN_E_INVALID and "flag" in text
 
 
@@ -312,6 +312,18 @@ def test_kv_token_stride_limit():
     d = good(B=1, k=(300 * lim, lim, 128), v=(300 * lim, lim, 128))
     st, text = B.validate_bwd(d)
     assert st == B.ATTN_E_WORKSPACE, text
+
+
+def test_log_route_flag_accepted_and_unknown_bits_rejected():
+    """ATTN_LOG_ROUTE is a known flag (validation goes on to the missing
+    workspace); bit 4 is not."""
+    seg = B.attn_segments(0x1000, None, None, None)
+    st, text = B.validate_fwd(good(flags=B.ATTN_LOG_ROUTE), seg)
+    assert st == B.ATTN_E_WORKSPACE, text
+    st, text = B.validate_bwd(good(flags=B.ATTN_LOG_ROUTE | B.ATTN_FORCE_GENERAL), seg)
+    assert st == B.ATTN_E_WORKSPACE, text
+    st, text = B.validate_fwd(good(flags=1 << 4), seg)
+    assert st == B.ATTN_E_INVALID and "unknown flag" in text, text
 
 
 def test_disjoint_packed_views_pass_the_stride_check():

@@ -246,3 +246,40 @@ def test_walks_longer_than_class_table(Sq, Skv, Hq, Hkv):
     assert gpu["route"] == "general"
     ref = G.run_oracle(case)
     G.check_all(case, gpu, ref)
+
+
+def test_log_route_reports_downgrades(capfd):
+    """ATTN_LOG_ROUTE writes one stderr line per batch row that the device
+    moved from the requested fast route to the general one (cross metadata
+    that differ from Q's), in the forward and in the backward's prepare
+    phase, and nothing for rows that keep the fast route (TransformerEngine
+    PR 3516, review: a warning when the fast path is not taken)."""
+    import torch
+    import bwd_packed_segments_amd as bps
+    cross = inputs.make_case(inputs.workload("thd_cross_ring_4k", B=2, Sq=600, Skv=600, Hq=2, Hkv=1, Dqk=64, Dv=64,
+                                             seg_lo=50, seg_hi=300), 4)
+    packed = inputs.make_case(inputs.workload("thd_packed_8k", B=2, S=600, Hq=2, Hkv=2, Dqk=64, Dv=64, seg_lo=50,
+                                              seg_hi=300), 4)
+    for name, case, expect_moved in (("cross", cross, None), ("packed", packed, 0)):
+        print(f"[log route] {name}", flush=True)
+        t = {k: G.to_dev(case[k], "bf16") for k in ("q", "k", "v", "do")}
+        seg = G.seg_to_dev(case["segments"])
+        capfd.readouterr()
+        o, lse, req, rows = bps.attn_fwd(t["q"], t["k"], t["v"], causal=case["causal"], segments=seg,
+                                         flags=bps.ATTN_LOG_ROUTE, return_route=True, return_route_rows=True)
+        torch.cuda.synchronize()
+        err_f = capfd.readouterr().err
+        bps.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=case["causal"], segments=seg,
+                     flags=bps.ATTN_LOG_ROUTE)
+        torch.cuda.synchronize()
+        err_b = capfd.readouterr().err
+        moved = int((rows.cpu().numpy() == 2).sum())
+        assert req == "fast"
+        if expect_moved is not None:
+            assert moved == expect_moved
+        else:
+            assert moved > 0
+        for err, call in ((err_f, "forward"), (err_b, "backward")):
+            lines = [l for l in err.splitlines() if "takes the general route" in l]
+            assert len(lines) == moved, (call, err)
+            assert all(f"bps_attn: {call}:" in l for l in lines), err
