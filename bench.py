@@ -42,7 +42,7 @@ PEAK_FP32_TFLOPS = 157.3
 METRIC = "fwd+bwd attention TFLOP/s (bf16) and % of MI355X MFMA peak, 1 GPU"
 DEFAULT_WORKLOAD = "gqa_causal_8k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["bps_common.hpp", "lds_tile.hpp", "attn_kernels.hpp", "dkdv_gs.hpp", "fwd_pp.hpp", "attn_inst.hip"]
+KERNEL_SOURCES = ["bps_common.hpp", "lds_tile.hpp", "attn_kernels.hpp", "dkdv_gs.hpp", "fwd_pp.hpp", "dq_hp.hpp", "attn_inst.hip"]
 
 
 # ------------------------------------------------------------------ counting
@@ -342,7 +342,7 @@ def ingest_counters(d, workload):
         out = {}
         with open(os.path.join(d, f"{tag}_counter_collection.csv")) as f:
             for r in csv.DictReader(f):
-                m = re.search(r"(attn_[a-z_]+?)(?:_ws|_gs|_pp)?_kernel", r["Kernel_Name"])
+                m = re.search(r"(attn_[a-z_]+?)(?:_ws|_gs|_pp|_hp)?_kernel", r["Kernel_Name"])
                 name = m.group(1) if m else ("copy" if "copy" in r["Kernel_Name"] else None)
                 if name:
                     out.setdefault(name, []).append(float(r["Counter_Value"]))

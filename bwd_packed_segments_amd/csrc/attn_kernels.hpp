@@ -1759,6 +1759,7 @@ __global__ void __launch_bounds__(2 * DQK) attn_bwd_dq_reduce_kernel(BwdArgs a) 
 
 #include "dkdv_gs.hpp"
 #include "fwd_pp.hpp"
+#include "dq_hp.hpp"
 
 namespace bps {
 
@@ -1886,6 +1887,16 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   if (nblocks <= 0) return hipSuccess;
   if constexpr (!VAR && DqCfg<T, DQK, DV, 8>::WIDE_OK) {
     if ((a.s.Hq / a.s.Hkv) % 2 == 0) {   // head pairs of a GQA group
+      if constexpr (sizeof(T) == 2 && DqHpCfg<DQK, DV>::ENABLED) {
+        const int64_t lim = (int64_t)1 << 31;
+        if (a.sk.t >= 0 && a.sv.t >= 0 && ((int64_t)(a.s.Skv - 1) * a.sk.t + DQK) * 2 < lim &&
+            ((int64_t)(a.s.Skv - 1) * a.sv.t + DV) * 2 < lim) {   // rotated blocks, three stages
+          using CP = DqHpCfg<DQK, DV>;
+          const long long nbp = (long long)a.s.B * (a.s.Hq / 2) * ((a.s.Sq + CP::BM - 1) / CP::BM);
+          hipLaunchKernelGGL((attn_bwd_dq_hp_kernel<DQK, DV>), dim3((unsigned)nbp), dim3(CP::THREADS), 0, st, a);
+          return hipGetLastError();
+        }
+      }
       using C8 = DqCfg<T, DQK, DV, 8, 2>;
       const long long nb8 = (long long)a.s.B * (a.s.Hq / 2) * ((a.s.Sq + C8::BM - 1) / C8::BM);
       hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV, false, 8, 2>), dim3((unsigned)nb8), dim3(C8::THREADS), 0, st,
