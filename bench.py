@@ -150,7 +150,7 @@ def variant_tensors(w, variant, seed=0):
     return out
 
 
-def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
+def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0, serial_bwd=False):
     import torch
     import bwd_packed_segments_amd as bps
 
@@ -172,6 +172,16 @@ def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
     bwd = bps.BwdPlan(dev["q"], dev["k"], dev["v"], fwd.o, fwd.lse, dev["do"], causal=w.causal, segments=seg,
                       flags=flags, **bwd_var)
     stream = torch.cuda.current_stream()
+    # dK/dV and dQ read the prepared workspace and write different outputs,
+    # so they may run at the same time (not under ATTN_FUSED_BWD, where dQ
+    # sums the partials dK/dV writes): dQ on a second stream of default
+    # priority, joined before the step ends.  Each fills the CUs the other's
+    # last workgroups leave idle.
+    can_overlap = not serial_bwd and not (flags & bps.ATTN_FUSED_BWD)
+    side = torch.cuda.Stream() if can_overlap else None
+    forked = torch.cuda.Event() if can_overlap else None
+    joined = torch.cuda.Event() if can_overlap else None
+    concurrent = False
 
     def step(ev=None):
         if ev is not None:
@@ -182,6 +192,23 @@ def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
         bwd.run(bps.ATTN_BWD_PREPARE)
         if ev is not None:
             ev[2].record(stream)
+        if concurrent:
+            forked.record(stream)
+            side.wait_event(forked)
+            with torch.cuda.stream(side):
+                if ev is not None:
+                    ev[5].record(side)
+                bwd.run(bps.ATTN_BWD_DQ)
+                if ev is not None:
+                    ev[6].record(side)
+                joined.record(side)
+            bwd.run(bps.ATTN_BWD_DKDV)
+            if ev is not None:
+                ev[3].record(stream)
+            stream.wait_event(joined)
+            if ev is not None:
+                ev[4].record(stream)
+            return
         bwd.run(bps.ATTN_BWD_DKDV)
         if ev is not None:
             ev[3].record(stream)
@@ -191,12 +218,33 @@ def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
 
     for _ in range(warmup):
         step()
+    # Two legal schedules of the backward phases: one stream, or dQ beside
+    # dK/dV.  Where the grids fill the GPU they take the same time and the
+    # overlap only blurs each kernel's own launch time (the roofline), so
+    # the second stream is used only when it is clearly faster here.
+    schedule = None
+    if can_overlap and warmup > 0:
+        def timed(conc, n=4):
+            nonlocal concurrent
+            concurrent = conc
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            step()
+            a.record(stream)
+            for _ in range(n):
+                step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+        t_ser = min(timed(False), timed(False))
+        t_con = min(timed(True), timed(True))
+        concurrent = t_con < 0.97 * t_ser
+        schedule = {"one_stream_ms": round(t_ser, 4), "two_streams_ms": round(t_con, 4)}
     # The route each batch row took on the device (the metadata check may
     # send a row that the host requested on the fast route to the general
     # one); read once, before the timed region.
     rows = bps.route_counts(bwd.route_rows()) if warmup > 0 else None
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -208,13 +256,13 @@ def run_gpu(w, steps, warmup, seed=0, variant=(), flags=0):
         phases["fwd"].append(ev[0].elapsed_time(ev[1]))
         phases["prepare"].append(ev[1].elapsed_time(ev[2]))
         phases["dkdv"].append(ev[2].elapsed_time(ev[3]))
-        phases["dq"].append(ev[3].elapsed_time(ev[4]))
+        phases["dq"].append(ev[5].elapsed_time(ev[6]) if concurrent else ev[3].elapsed_time(ev[4]))
         phases["step"].append(ev[0].elapsed_time(ev[4]))
     avg = {k: float(np.mean(v)) for k, v in phases.items()}
     med = {k: float(np.median(v)) for k, v in phases.items()}
     if rows is None:
         rows = bps.route_counts(bwd.route_rows())
-    return case, wall, avg, med, (fwd.route, rows)
+    return case, wall, avg, med, (fwd.route, rows), (2 if concurrent else 1, schedule)
 
 
 def ring_bench(w, cp, steps, warmup, seed=0):
@@ -240,6 +288,27 @@ def ring_bench(w, cp, steps, warmup, seed=0):
 
     for _ in range(warmup):
         step()
+    # Two legal schedules of the backward phases: one stream, or dQ beside
+    # dK/dV.  Where the grids fill the GPU they take the same time and the
+    # overlap only blurs each kernel's own launch time (the roofline), so
+    # the second stream is used only when it is clearly faster here.
+    schedule = None
+    if can_overlap and warmup > 0:
+        def timed(conc, n=4):
+            nonlocal concurrent
+            concurrent = conc
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            step()
+            a.record(stream)
+            for _ in range(n):
+                step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+        t_ser = min(timed(False), timed(False))
+        t_con = min(timed(True), timed(True))
+        concurrent = t_con < 0.97 * t_ser
+        schedule = {"one_stream_ms": round(t_ser, 4), "two_streams_ms": round(t_con, 4)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -395,6 +464,9 @@ def main():
     ap.add_argument("--fused-bwd", action="store_true",
                     help="time the single-pass backward (ATTN_FUSED_BWD): the dK/dV kernel also writes dQ "
                          "partials, the dQ phase sums them in key-tile order")
+    ap.add_argument("--serial-bwd", action="store_true",
+                    help="run the dK/dV and dQ phases one after the other on one stream (default: dQ on a second "
+                         "stream beside dK/dV)")
     ap.add_argument("--force-general", action="store_true",
                     help="set ATTN_FORCE_GENERAL: run workloads with segment metadata on the general route even "
                          "where the fast route applies (what the fast path saves)")
@@ -439,7 +511,8 @@ def main():
         raise SystemExit("--fused-bwd takes no bias or soft cap")
     import bwd_packed_segments_amd as bps
     flags = (bps.ATTN_FUSED_BWD if args.fused_bwd else 0) | (bps.ATTN_FORCE_GENERAL if args.force_general else 0)
-    case, wall, avg, med, (route_req, route_rows) = run_gpu(w, args.steps, args.warmup, variant=variant, flags=flags)
+    case, wall, avg, med, (route_req, route_rows), (bwd_streams, schedule) = run_gpu(
+        w, args.steps, args.warmup, variant=variant, flags=flags, serial_bwd=args.serial_bwd)
     route = next(iter(route_rows)) if len(route_rows) == 1 else "mixed"
     n = allowed_pairs(w, case["segments"])
     F = flops(w, n)
@@ -495,7 +568,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal, "metadata": w.meta, "route": route,
                    "route_requested": route_req, "route_rows": route_rows,
-                   "allowed_pairs": n, "flop_per_step": f_step},
+                   "allowed_pairs": n, "flop_per_step": f_step,
+                   "bwd_streams": bwd_streams, "bwd_schedule_probe_ms": schedule},
         "pct_peak": round(100.0 * value / peak, 2),
         "phase_ms": {k: round(v, 4) for k, v in avg.items()},
         "phase_ms_median": {k: round(v, 4) for k, v in med.items()},
