@@ -288,27 +288,6 @@ def ring_bench(w, cp, steps, warmup, seed=0):
 
     for _ in range(warmup):
         step()
-    # Two legal schedules of the backward phases: one stream, or dQ beside
-    # dK/dV.  Where the grids fill the GPU they take the same time and the
-    # overlap only blurs each kernel's own launch time (the roofline), so
-    # the second stream is used only when it is clearly faster here.
-    schedule = None
-    if can_overlap and warmup > 0:
-        def timed(conc, n=4):
-            nonlocal concurrent
-            concurrent = conc
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            step()
-            a.record(stream)
-            for _ in range(n):
-                step()
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / n
-        t_ser = min(timed(False), timed(False))
-        t_con = min(timed(True), timed(True))
-        concurrent = t_con < 0.97 * t_ser
-        schedule = {"one_stream_ms": round(t_ser, 4), "two_streams_ms": round(t_con, 4)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):

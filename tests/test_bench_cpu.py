@@ -42,3 +42,25 @@ def test_multi_gpu_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
                        cwd=bench.ROOT)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bench_functions_name_only_defined_globals():
+    """Every global name a function in bench.py reads is bound at module
+    level or is a builtin (a name left over from another function's body
+    would only fail on the GPU, in the middle of a run)."""
+    import builtins
+    import symtable
+    with open(bench.__file__) as f:
+        table = symtable.symtable(f.read(), bench.__file__, "exec")
+    known = set(vars(bench)) | set(dir(builtins))
+    missing = []
+
+    def walk(t):
+        if t.get_type() == "function":
+            for s in t.get_symbols():
+                if s.is_referenced() and s.is_global() and s.get_name() not in known:
+                    missing.append(f"{t.get_name()}: {s.get_name()}")
+        for c in t.get_children():
+            walk(c)
+    walk(table)
+    assert not missing, missing
