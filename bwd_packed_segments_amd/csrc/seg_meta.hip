@@ -29,6 +29,50 @@ constexpr int kSegWaves = kSegThreads / 64;
 
 __device__ inline int op_max(int a, int b) { return a > b ? a : b; }
 __device__ inline int op_min(int a, int b) { return a < b ? a : b; }
+// Token index i clamped into [0, S) (S >= 1): loads of a round are issued
+// unconditionally at clamped indices and out-of-row items ignore the value,
+// so no load sits behind a per-lane branch.
+__device__ inline int clamp_tok(int i, int S) { return i < 0 ? 0 : (i < S ? i : S - 1); }
+
+// One thread's tokens base .. base + 7 of a row.  All of a row passes
+// through one CU, so the loads and stores are 16 bytes per lane where the
+// row start is 16-byte aligned (base is a multiple of 8) and the eight
+// tokens are inside the row; elsewhere element accesses (loads at clamped
+// indices, stores only inside the row).
+__device__ inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+__device__ inline void load8(const int* p, int base, int S, bool vec, int (&o)[kSegItems]) {
+  if (vec && base + kSegItems <= S) {
+    const int4 x = *reinterpret_cast<const int4*>(p + base);
+    const int4 y = *reinterpret_cast<const int4*>(p + base + 4);
+    o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    o[4] = y.x; o[5] = y.y; o[6] = y.z; o[7] = y.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k) o[k] = p[clamp_tok(base + k, S)];
+  }
+}
+__device__ inline void store8(int* p, int base, int S, bool vec, const int (&v)[kSegItems]) {
+  if (vec && base + kSegItems <= S) {
+    *reinterpret_cast<int4*>(p + base) = make_int4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<int4*>(p + base + 4) = make_int4(v[4], v[5], v[6], v[7]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k)
+      if (base + k < S) p[base + k] = v[k];
+  }
+}
+__device__ inline void store8_run(int2* p, int base, int S, bool vec, const int (&x)[kSegItems],
+                                  const int (&y)[kSegItems]) {
+  if (vec && base + kSegItems <= S) {
+#pragma unroll
+    for (int k = 0; k < kSegItems; k += 2)
+      *reinterpret_cast<int4*>(p + base + k) = make_int4(x[k], y[k], x[k + 1], y[k + 1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k)
+      if (base + k < S) p[base + k] = make_int2(x[k], y[k]);
+  }
+}
 
 // Exclusive scan over the threads of the workgroup: forward combines the
 // values of threads before this one, reverse those after it.  Returns the
@@ -81,6 +125,12 @@ __global__ __launch_bounds__(kSegThreads) void seg_meta_kernel(SegMetaArgs a) {
   int ok = 1;
   int carry_start = -1;
   int carry_nz = INT32_MIN;
+  // Phase 1's last round is the round phase 2 starts with: its ids, next
+  // id, positions and run starts stay in registers.
+  int rs_last[kSegItems], id_last[kSegItems], pin_last[kSegItems], next_last = 0;
+  const bool vec_ids = al16(ids), vec_run = al16(run);
+  const bool vec_pin = pos_in && al16(pos_in), vec_pout = pos_out && al16(pos_out);
+  const bool vec_ikv = ids_kv && al16(ids_kv), vec_pkv = pos_kv && al16(pos_kv);
   const int nrounds = (S + kSegRound - 1) / kSegRound;
 
   // Phase 1, left to right: run starts, derived positions, fast-route checks.
@@ -88,14 +138,23 @@ __global__ __launch_bounds__(kSegThreads) void seg_meta_kernel(SegMetaArgs a) {
     const int base = rd * kSegRound + t * kSegItems;
     int id[kSegItems];
     int st[kSegItems];
-    int prev = (base > 0 && base - 1 < S) ? ids[base - 1] : 0;
+    // Every load of the round is issued here, before the scans' barriers
+    // (which loads cannot move across), and waited for once.
+    const int prev_v = ids[clamp_tok(base - 1, S)];
+    const int next_v = ids[clamp_tok(base + kSegItems, S)];
+    int prev = (base > 0 && base - 1 < S) ? prev_v : 0;
+    load8(ids, base, S, vec_ids, id);
+    int pin[kSegItems], ikv[kSegItems], pkv[kSegItems];
+    if (pos_in) load8(pos_in, base, S, vec_pin, pin);
+    if (eq_check) load8(ids_kv, base, S, vec_ikv, ikv);
+    if (pos_kv) load8(pos_kv, base, S, vec_pkv, pkv);
     int st_local = -1;
     int nz_local = INT32_MIN;
 #pragma unroll
     for (int k = 0; k < kSegItems; ++k) {
       const int i = base + k;
       const bool in = i < S;
-      id[k] = in ? ids[i] : 0;
+      if (!in) id[k] = 0;
       const int pid = k == 0 ? prev : id[k - 1];
       if (in && (i == 0 || id[k] != pid)) st_local = i;
       st[k] = st_local;
@@ -108,38 +167,69 @@ __global__ __launch_bounds__(kSegThreads) void seg_meta_kernel(SegMetaArgs a) {
     carry_nz = op_max(carry_nz, tot);
     bool seen_nz = pre_nz != INT32_MIN;
     int running_nz = pre_nz;
+    int rsv[kSegItems];
 #pragma unroll
     for (int k = 0; k < kSegItems; ++k) {
       const int i = base + k;
-      if (i >= S) break;
-      const int rs = st[k] >= 0 ? st[k] : pre_start;
-      const int dpos = i - rs;
-      if (id[k] != 0) {
-        if (id[k] == INT32_MIN) ok = 0;
-        if (rs == i && seen_nz && id[k] <= running_nz) ok = 0;
-        running_nz = seen_nz ? op_max(running_nz, id[k]) : id[k];
-        seen_nz = true;
+      rsv[k] = st[k] >= 0 ? st[k] : pre_start;
+      if (i < S) {
+        const int rs = rsv[k];
+        const int dpos = i - rs;
+        if (id[k] != 0) {
+          if (id[k] == INT32_MIN) ok = 0;
+          if (rs == i && seen_nz && id[k] <= running_nz) ok = 0;
+          running_nz = seen_nz ? op_max(running_nz, id[k]) : id[k];
+          seen_nz = true;
+        }
+        const int p = pos_in ? pin[k] : dpos;
+        if (pos_in && id[k] != 0 && p != dpos) ok = 0;
+        if (eq_check) {
+          const int pk = pos_kv ? pkv[k] : dpos;
+          if (ikv[k] != id[k] || pk != p) ok = 0;
+        }
       }
-      const int p = pos_in ? pos_in[i] : dpos;
-      if (pos_in && id[k] != 0 && p != dpos) ok = 0;
-      if (pos_out) pos_out[i] = dpos;
-      if (eq_check) {
-        const int pk = pos_kv ? pos_kv[i] : dpos;
-        if (ids_kv[i] != id[k] || pk != p) ok = 0;
-      }
-      run[i] = make_int2(rs, 0);
     }
+    // The round's stores last, back to back (a store waited for before the
+    // next token's work would cost a round trip per token again).
+    int dpv[kSegItems], zero[kSegItems];
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k) {
+      rs_last[k] = rsv[k];
+      id_last[k] = id[k];
+      pin_last[k] = pos_in ? pin[k] : 0;
+      dpv[k] = base + k - rsv[k];
+      zero[k] = 0;
+    }
+    next_last = base + kSegItems < S ? next_v : 0;
+    if (pos_out) store8(pos_out, base, S, vec_pout, dpv);
+    store8_run(run, base, S, vec_run, rsv, zero);
   }
 
   // Phase 2, right to left: run ends, final run bounds, 32-token summaries.
   int carry_end = INT32_MAX;
   for (int rd = nrounds - 1; rd >= 0; --rd) {
     const int base = rd * kSegRound + t * kSegItems;
-    int id[kSegItems];
-    int en[kSegItems];
+    int id[kSegItems], en[kSegItems], rsv[kSegItems], pin[kSegItems];
+    int next;
+    if (rd == nrounds - 1) {
 #pragma unroll
-    for (int k = 0; k < kSegItems; ++k) id[k] = (base + k < S) ? ids[base + k] : 0;
-    const int next = (base + kSegItems < S) ? ids[base + kSegItems] : 0;
+      for (int k = 0; k < kSegItems; ++k) {
+        id[k] = id_last[k];
+        rsv[k] = rs_last[k];
+        pin[k] = pin_last[k];
+      }
+      next = next_last;
+    } else {   // a whole round: ids, positions and run starts (this thread's own phase-1 stores)
+      load8(ids, base, S, vec_ids, id);
+      const int next_v = ids[clamp_tok(base + kSegItems, S)];
+#pragma unroll
+      for (int k = 0; k < kSegItems; ++k) rsv[k] = run[clamp_tok(base + k, S)].x;
+      if (pos_in) load8(pos_in, base, S, vec_pin, pin);
+#pragma unroll
+      for (int k = 0; k < kSegItems; ++k)
+        if (base + k >= S) id[k] = 0;
+      next = base + kSegItems < S ? next_v : 0;
+    }
     int en_local = INT32_MAX;
 #pragma unroll
     for (int k = kSegItems - 1; k >= 0; --k) {
@@ -156,24 +246,29 @@ __global__ __launch_bounds__(kSegThreads) void seg_meta_kernel(SegMetaArgs a) {
 
     int cnt = 0, idmin = INT32_MAX, idmax = INT32_MIN, pmin = INT32_MAX, pmax = INT32_MIN;
     int smin = INT32_MAX, smax = INT32_MIN, emin = INT32_MAX, emax = INT32_MIN;
+    int rev[kSegItems];
 #pragma unroll
     for (int k = 0; k < kSegItems; ++k) {
       const int i = base + k;
-      if (i >= S) break;
-      if (id[k] == 0) {
-        run[i] = make_int2(0, 0);
-        continue;
+      rev[k] = en[k] != INT32_MAX ? en[k] : pre_end;
+      if (i < S && id[k] != 0) {
+        const int rs = rsv[k];
+        const int re = rev[k];
+        const int p = pos_in ? pin[k] : i - rs;
+        ++cnt;
+        idmin = op_min(idmin, id[k]); idmax = op_max(idmax, id[k]);
+        pmin = op_min(pmin, p); pmax = op_max(pmax, p);
+        smin = op_min(smin, rs); smax = op_max(smax, rs);
+        emin = op_min(emin, re); emax = op_max(emax, re);
       }
-      const int rs = run[i].x;
-      const int re = en[k] != INT32_MAX ? en[k] : pre_end;
-      run[i] = make_int2(rs, re);
-      const int p = pos_in ? pos_in[i] : i - rs;
-      ++cnt;
-      idmin = op_min(idmin, id[k]); idmax = op_max(idmax, id[k]);
-      pmin = op_min(pmin, p); pmax = op_max(pmax, p);
-      smin = op_min(smin, rs); smax = op_max(smax, rs);
-      emin = op_min(emin, re); emax = op_max(emax, re);
     }
+    int rso[kSegItems], reo[kSegItems];
+#pragma unroll
+    for (int k = 0; k < kSegItems; ++k) {
+      rso[k] = id[k] != 0 ? rsv[k] : 0;
+      reo[k] = id[k] != 0 ? rev[k] : 0;
+    }
+    store8_run(run, base, S, vec_run, rso, reo);
     // 4 consecutive threads cover one 32-token chunk.
 #pragma unroll
     for (int d = 1; d < 4; d <<= 1) {
