@@ -1662,12 +1662,24 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 
 // dK (times the softmax scale) and dV of one key tile from the kv_split
 // partials of its split walk, added in split order.  One wave per 32-key
-// block, each lane the C-layout values the consumer wave held.
+// block, each lane the C-layout values the consumer wave held; blockIdx.y
+// picks 4 of the tile's float4 slots per lane, so that the grid has enough
+// waves and each lane enough loads in flight (all splits' loads are issued
+// first, at a clamped split index, and only the real ones are added).
+constexpr int kReduceSlots = 4;   // float4 slots per lane and workgroup
+constexpr int kReduceMaxSplit = 4;
+
+template <int DQK, int DV>
+constexpr int dkdv_reduce_chunks() {
+  return 4 * (DQK / 32 + DV / 32) / kReduceSlots;
+}
+
 template <typename T, int DQK, int DV>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_reduce_kernel(BwdArgs a) {
   using E = Elem<T>;
   constexpr int BN = DkvWsCfg<T, DQK, DV>::BN;
   constexpr int NF4 = 4 * (DQK / 32 + DV / 32);
+  static_assert(NF4 % kReduceSlots == 0, "slots split evenly");
   const AttnShape& s = a.s;
   const int nsplit = a.kv_split;
   const int n_kt = (s.Skv + BN - 1) / BN;
@@ -1681,16 +1693,25 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_reduce_kernel(BwdArgs a) {
   const int n = lane & 31;
   const int hf = lane >> 5;
   const int kj = krank * BN + kb * 32 + n;
+  const int i0 = blockIdx.y * kReduceSlots;
   const size_t stride = (size_t)4 * NF4 * 64;   // between the partials of consecutive splits
   const f32x4* part = reinterpret_cast<const f32x4*>(a.dkvp) +
                       (((size_t)b * s.Hkv + hkv) * n_kt + krank) * nsplit * stride + (size_t)kb * NF4 * 64 + lane;
   if (kj >= s.Skv) return;
+  f32x4 x[kReduceMaxSplit][kReduceSlots];
+#pragma unroll
+  for (int sp = 0; sp < kReduceMaxSplit; ++sp)
+#pragma unroll
+    for (int j = 0; j < kReduceSlots; ++j) x[sp][j] = part[(sp < nsplit ? sp : 0) * stride + (i0 + j) * 64];
   T* dkp = static_cast<T*>(a.dk) + b * a.sk.b + kj * a.sk.t + hkv * a.sk.h;
   T* dvp = static_cast<T*>(a.dv) + b * a.sv.b + kj * a.sv.t + hkv * a.sv.h;
-#pragma unroll 4
-  for (int i = 0; i < NF4; ++i) {
-    f32x4 v = part[i * 64];
-    for (int sp = 1; sp < nsplit; ++sp) v += part[sp * stride + i * 64];
+#pragma unroll
+  for (int j = 0; j < kReduceSlots; ++j) {
+    f32x4 v = x[0][j];
+#pragma unroll
+    for (int sp = 1; sp < kReduceMaxSplit; ++sp)
+      if (sp < nsplit) v += x[sp][j];
+    const int i = i0 + j;
     const int d = (i >> 2) % (DQK / 32), grp = i & 3;
     if (i < 4 * (DQK / 32))
       *reinterpret_cast<typename E::P4*>(dkp + d * 32 + 8 * grp + 4 * hf) = E::cvt4(v * s.scale);
@@ -1827,7 +1848,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
   const int n_kt = (a.s.Skv + DkvCfg<T, DQK, DV>::BN - 1) / DkvCfg<T, DQK, DV>::BN;
   const long long nblocks = (long long)a.s.B * a.s.Hkv * n_kt;
   if (nblocks <= 0) return hipSuccess;
-  if (a.kv_split < 1 || (a.kv_split > 1 && (!DkvWsCfg<T, DQK, DV>::ENABLED || a.dkvp == nullptr)))
+  if (a.kv_split < 1 || a.kv_split > kReduceMaxSplit ||
+      (a.kv_split > 1 && (!DkvWsCfg<T, DQK, DV>::ENABLED || a.dkvp == nullptr)))
     return hipErrorInvalidValue;
   const unsigned nws = (unsigned)(nblocks * a.kv_split);
   const bool split = a.kv_split > 1;
@@ -1865,7 +1887,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
     if (a.kv_split > 1) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_bwd_dkdv_reduce_kernel<T, DQK, DV>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_bwd_dkdv_reduce_kernel<T, DQK, DV>),
+                         dim3((unsigned)nblocks, (unsigned)dkdv_reduce_chunks<DQK, DV>()), dim3(256), 0, st, a);
     }
   }
   return hipGetLastError();
