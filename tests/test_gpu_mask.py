@@ -68,6 +68,46 @@ def test_debug_mask_bit_exact(name, seg, Sq, Skv, causal, force_general):
     assert np.array_equal(routes.cpu().numpy(), np.where(expect, 1, 2))
 
 
+def _at_offset(x, off):
+    """x as a contiguous int32 device tensor that starts `off` int32 past a
+    16-byte boundary (a view into a larger buffer)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.int32)
+    buf = torch.zeros(x.size + 4, dtype=torch.int32, device="cuda")
+    assert buf.data_ptr() % 16 == 0
+    v = buf[off:off + x.size].view(x.shape)
+    v.copy_(torch.from_numpy(x).to("cuda"))
+    return v
+
+
+@pytest.mark.parametrize("off", [1, 2, 3])
+@pytest.mark.parametrize("sep", [False, True])
+def test_metadata_at_unaligned_addresses(off, sep):
+    """Metadata tensors 4, 8 or 12 bytes past a 16-byte boundary: the metadata
+    kernel reads and writes them element by element instead of 16 bytes at a
+    time, and the mask and the routes are still the oracle's, bit for bit."""
+    import bwd_packed_segments_amd as bps
+    import torch
+    w = inputs.workload("thd_packed_8k", B=2, S=1000, seg_lo=20, seg_hi=300)
+    seg = inputs.segments_for(w, 6)
+    if sep:   # equal metadata in separate KV buffers: fast after the device compare
+        seg = {"ids_q": seg["ids_q"], "pos_q": seg["pos_q"], "ids_kv": seg["ids_q"].copy(),
+               "pos_kv": seg["pos_q"].copy()}
+    print(f"[mask] unaligned metadata off={off} sep={sep}", flush=True)
+    dev = bps.Segments(*[None if seg.get(k) is None else _at_offset(seg[k], off)
+                         for k in ("ids_q", "pos_q", "ids_kv", "pos_kv")])
+    assert dev.ids_q.data_ptr() % 16 == 4 * off
+    for causal in (True, False):
+        mask, routes = bps.attn_debug_mask(B=2, Sq=1000, Skv=1000, causal=causal, segments=dev)
+        torch.cuda.synchronize()
+        res = oracle.resolve_segments(seg, 2, 1000, 1000)
+        for b in range(2):
+            ref = oracle.allowed_mask(b, 1000, 1000, causal, res)
+            assert np.array_equal(mask[b].cpu().numpy().astype(bool), ref), f"row {b} causal={causal}"
+        expect = oracle.fast_route_eligible(seg, 2, 1000, 1000)
+        assert np.array_equal(routes.cpu().numpy(), np.where(expect, 1, 2))
+
+
 def test_debug_mask_dense():
     import bwd_packed_segments_amd as bps
     import torch

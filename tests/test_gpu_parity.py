@@ -76,6 +76,21 @@ def test_head_dims_fp32(dqk, dv, causal):
     _parity(case)
 
 
+@pytest.mark.parametrize("S,H,causal,parts", [(1024, 50, True, 2), (1024, 32, False, 3)])
+def test_split_dkdv_walks(S, H, causal, parts):
+    """bf16 dK/dV grids of fewer than 512 key tiles cut each key tile's walk
+    over query tiles into parts whose fp32 partials a second kernel adds in
+    part order.  These shapes (400 and 256 key tiles) take 2 and 3 parts; the
+    workspace, which holds one partial per part, shows which."""
+    from bwd_packed_segments_amd import binding
+    n_kt = H * ((S + 127) // 128)
+    per_part = n_kt * 128 * (128 + 128) * 4
+    ws = binding.bwd_workspace_size(binding.make_desc(B=1, Sq=S, Skv=S, Hq=H, Hkv=H, Dqk=128, Dv=128, causal=causal))
+    assert parts * per_part <= ws < (parts + 1) * per_part
+    case = G.small_case("bshd_causal_2k", 15, B=1, S=S, Hq=H, Hkv=H, causal=causal)
+    _parity(case)
+
+
 def test_odd_lengths_cross():
     """Non-divisible lengths (1350 queries, 1777 keys), GQA."""
     case = G.small_case("thd_cross_ring_4k", 5, Sq=1350, Skv=1777, Hq=4, Hkv=2, Dqk=128, seg_lo=64, seg_hi=700)
