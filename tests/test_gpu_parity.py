@@ -76,6 +76,19 @@ def test_head_dims_fp32(dqk, dv, causal):
     _parity(case)
 
 
+@pytest.mark.parametrize("dqk,dv", [(128, 128), (64, 64), (128, 64)])
+@pytest.mark.parametrize("force_general", [False, True])
+def test_packed_gqa(dqk, dv, force_general):
+    """Packed self-attention with GQA groups of 4, causal inside segments:
+    the head-pair forward and dQ and the gradient-split dK/dV with segment
+    boundaries inside their tiles, on the fast route and with every row
+    forced onto the general one."""
+    import bwd_packed_segments_amd as bps
+    case = G.small_case("thd_packed_8k", 16, B=2, S=700, Hq=8, Hkv=2, Dqk=dqk, Dv=dv, seg_lo=16, seg_hi=300)
+    stats, gpu, _ = _parity(case, flags=bps.ATTN_FORCE_GENERAL if force_general else 0)
+    assert gpu["route"] == ("general" if force_general else "fast")
+
+
 @pytest.mark.parametrize("S,H,causal,parts", [(1024, 50, True, 2), (1024, 32, False, 3)])
 def test_split_dkdv_walks(S, H, causal, parts):
     """bf16 dK/dV grids of fewer than 512 key tiles cut each key tile's walk
