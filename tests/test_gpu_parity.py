@@ -89,6 +89,24 @@ def test_packed_gqa(dqk, dv, force_general):
     assert gpu["route"] == ("general" if force_general else "fast")
 
 
+def test_many_batch_rows_packed():
+    """Sixteen batch rows of packed segments (one metadata workgroup and one
+    route per row), GQA groups of 2, causal inside segments."""
+    case = G.small_case("thd_packed_8k", 17, B=16, S=300, Hq=4, Hkv=2, seg_lo=16, seg_hi=200)
+    stats, gpu, _ = _parity(case)
+    assert gpu["route"] == "fast"
+
+
+def test_cross_causal_unequal_lengths():
+    """Cross attention on the general route with Sq != Skv and a causal mask
+    over positions (allowed with metadata: causal compares positions, not
+    token indices), GQA groups of 2."""
+    case = G.small_case("thd_cross_ring_4k", 18, Sq=600, Skv=900, Hq=4, Hkv=2, Dqk=128, seg_lo=32, seg_hi=256,
+                        causal=True)
+    stats, gpu, _ = _parity(case)
+    assert gpu["route"] == "general"
+
+
 @pytest.mark.parametrize("S,H,causal,parts", [(1024, 50, True, 2), (1024, 32, False, 3)])
 def test_split_dkdv_walks(S, H, causal, parts):
     """bf16 dK/dV grids of fewer than 512 key tiles cut each key tile's walk
