@@ -11,7 +11,7 @@ import pytest
 import oracle
 from oracle import attention as oa
 from tests import oracle_pins as P
-from tests.test_oracle_pins import CASES
+from tests.test_oracle_pins import CASES, FAST
 
 SRC = open(os.path.join(os.path.dirname(oa.__file__), "attention.py")).read()
 
@@ -33,6 +33,12 @@ MUTATIONS = {
     "dq_uses_q": ("dQ[b, :, h, :] = scale * (dS @ kh)", "dQ[b, :, h, :] = scale * (dS @ qh)"),
     "derive_pos_off_by_one": ("pos[b, i] = i - start", "pos[b, i] = i - start + 1"),
     "max_unmasked": ("masked = np.where(mask, S, -np.inf)", "masked = S"),
+    "dk_overwrites_group": ("dK[b, :, c, :] += scale * (dS.T @ qh)", "dK[b, :, c, :] = scale * (dS.T @ qh)"),
+    "dv_overwrites_group": ("dV[b, :, c, :] += P.T @ doh", "dV[b, :, c, :] = P.T @ doh"),
+    "fast_route_nonstrict": ("if best is not None and cur <= best:", "if best is not None and cur < best:"),
+    "fast_route_ignores_pos": ("if cur != 0 and int(pos_q[b, i]) != i - start:", "if False:"),
+    "empty_row_lse_zero": ("lse = np.where(n > 0, m_safe + np.log(np.where(den > 0, den, 1.0)), -np.inf)",
+                           "lse = np.where(n > 0, m_safe + np.log(np.where(den > 0, den, 1.0)), 0.0)"),
 }
 
 
@@ -62,6 +68,10 @@ def _all_pins_pass():
                     segs["pos_kv"] = np.array([[int(x) for x in case["pos_kv"]]], dtype=np.int32)
                 seg = oracle.resolve_segments(segs, 1, Sq, Skv)
             if not np.array_equal(oracle.allowed_mask(0, Sq, Skv, causal, seg), mask):
+                return False
+        for flag, fids, fpos in FAST:
+            if bool(oracle.fast_route_eligible({"ids_q": fids[None], "pos_q": fpos[None]}, 1, fids.size,
+                                               fids.size)[0]) != bool(flag):
                 return False
         ids = np.array([[1, 1, 1, 2, 2, 0, 0, 3, 3, 1]], dtype=np.int32)
         if not np.array_equal(oracle.derive_pos(ids)[0], [0, 1, 2, 0, 1, 0, 1, 0, 1, 0]):
