@@ -28,6 +28,11 @@ MUTATIONS = {
     "dq_from_ds": ("dQ[b, :, h, :] = scale * (dX @ kh)", "dQ[b, :, h, :] = scale * (dS @ kh)"),
     "sink_lse_dropped": ("lse = np.where(live, m0 + np.log(den_safe), -np.inf)",
                          "lse = np.where(live, m0 + np.log(den_safe - e_sink + 1e-300), -np.inf)"),
+    "bias_after_softcap": ("    if bias_h is not None:\n        X = X + bias_h\n    if softcap:\n"
+                           "        S = softcap * np.tanh(X / softcap)\n    else:\n        S = X\n",
+                           "    if softcap:\n        S = softcap * np.tanh(X / softcap)\n    else:\n        S = X\n"
+                           "    if bias_h is not None:\n        X = X + bias_h\n        S = S + bias_h\n"),
+    "sink_base2": ("e_sink = np.exp(sink_h - m0)", "e_sink = np.exp2(sink_h - m0)"),
 }
 
 
